@@ -1,0 +1,162 @@
+/*
+ * hlwq.h — C ABI of libhlwq, the MI355X (gfx950) HLWQ quantize / dequantize
+ * library (Hadamard-Lloyd Weight Quantization).
+ *
+ * The method (model card "Qwen3.6-35B-A3B — HLWQ Q5", section "Method",
+ * steps [1]-[5]): view a weight matrix W (out x in) as (out, n_blocks, 128)
+ * with the last block zero-padded; L2-normalise every block and keep its norm
+ * as fp16 ("Gemma-4-26B-A4B-it-HLWQ-Q5", "Technical Details"); rotate each
+ * block by the orthonormal 128x128 Walsh-Hadamard matrix scaled by sqrt(128);
+ * replace every value by the index of the nearest of 2^bits Lloyd-Max
+ * centroids for N(0, 1); pack 8 codes into `bits` bytes.  Dequantisation is
+ * the inverse, written as bf16 ("Qwopus3.6-27B-v2 · HLWQ Q5", "Pipeline":
+ * dequantize per Linear to BF16).  The KV-cache path ("Qwopus3.6-27B-v2 ·
+ * HLWQ Q5", "Methodology notes", KV bullet) does the same per 256-wide head
+ * vector with H256 and 8 centroids, and leaves the newest tokens unquantised.
+ *
+ * Arithmetic.  Every kernel follows one fixed IEEE-fp32 operation order, so
+ * results are bit-identical run to run and device to device:
+ *   norm   : squares summed by an adjacent-pair tree, correctly rounded sqrt,
+ *            fp16 by round-to-nearest-even;
+ *   rotate : unnormalised +-1 butterflies (a, b) -> (a + b, a - b) at strides
+ *            1, 2, 4, ... (natural / Sylvester order), then y = z * (1 / n),
+ *            1 / n correctly rounded, and 0 for blocks whose norm is below the
+ *            smallest normal fp32 value (so a zero block gives y = 0);
+ *   code   : number of fp32 decision thresholds strictly below y, i.e. the
+ *            nearest fp32 centroid with ties to the lower index;
+ *   inverse: the same butterflies on the centroids, times n16 / L (L = 128 or
+ *            256, exact in fp32), rounded to bf16 nearest-even.
+ *
+ * Layouts (all row-major, contiguous, little-endian):
+ *   W        bf16 [n_mats][out][in]
+ *   packed   u8   [n_mats][out][nb][16 * bits], nb = ceil(in / 128); within a
+ *                 block, group g of 8 codes (positions 8g .. 8g+7) is the
+ *                 little-endian integer sum_i code_i << (bits * i) stored in
+ *                 bytes [g * bits, g * bits + bits)
+ *   norms    fp16 [n_mats][out][nb]
+ *   KV       bf16 [batch][heads][tokens][256]; packed u8 [batch][heads][tq][32 * bits]
+ *            and norms fp16 [batch][heads][tq] with tq = max(tokens - n_residual, 0)
+ *
+ * Ownership and execution: the caller allocates every buffer, in device
+ * memory of the current HIP device.  The library keeps no state beyond
+ * constant tables compiled into the code object and allocates nothing.  Every
+ * call validates its arguments on the host first; on success it enqueues the
+ * work on `hip_stream` (a hipStream_t; NULL means the default stream) and
+ * returns without synchronising.  Calls are reentrant; calls on different
+ * streams may run concurrently.
+ *
+ * Errors: every int-returning call returns HLWQ_OK (0) or a negative
+ * HLWQ_ERR_* status; nothing is enqueued on error and output buffers are left
+ * untouched.  Zero-sized work (n_mats, out, in, batch, heads or the quantised
+ * token count equal to 0) is valid, does nothing and accepts NULL pointers.
+ * Inputs must be finite; a block whose squared norm overflows fp32 (an entry
+ * above ~1.8e19 in magnitude) yields an infinite norm and unspecified codes.
+ *
+ * Alignment: `packed` must be 16-byte aligned, `norms` and bf16 buffers 2-byte
+ * aligned; W rows need no further alignment (rows whose start is not 16-byte
+ * aligned take a slower element-wise path).
+ */
+#ifndef HLWQ_H
+#define HLWQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  HLWQ_OK = 0,
+  HLWQ_ERR_NULL = -1,    /* a required pointer is NULL */
+  HLWQ_ERR_SHAPE = -2,   /* negative size, or a size whose byte count overflows int64 */
+  HLWQ_ERR_BITS = -3,    /* bits not supported for this call */
+  HLWQ_ERR_BLOCK = -4,   /* block != 128 (weights) or head_dim != 256 (KV) */
+  HLWQ_ERR_DEVICE = -5,  /* the HIP launch reported an error */
+  HLWQ_ERR_ALIGN = -6,   /* a buffer violates the alignment stated above */
+  HLWQ_ERR_LIMIT = -7    /* more than 2^31 - 1 blocks / vectors in one matrix or cache */
+};
+
+/* One matrix of a grouped call.  For hlwq_quantize_grouped `w` is read and
+ * `packed` / `norms` are written; for hlwq_dequantize_grouped `packed` /
+ * `norms` are read and `w` is written.  `rows` = n_mats * out of that matrix
+ * (an expert bank [E][out][in] is one descriptor with rows = E * out). */
+typedef struct hlwq_mat_desc {
+  void* w;        /* bf16 [rows][in] */
+  void* packed;   /* u8   [rows][nb][16 * bits] */
+  void* norms;    /* fp16 [rows][nb] */
+  int64_t rows;
+  int64_t in;
+} hlwq_mat_desc;
+
+/* Quantize W [n_mats][out][in] (bf16) with HLWQ, block = 128, bits = 5 (32
+ * centroids, Q5) or 3 (8 centroids, Q3): steps [1]-[5] of "Qwen3.6-35B-A3B —
+ * HLWQ Q5", section "Method".  Writes packed [n_mats][out][nb][16*bits] and
+ * fp16 norms [n_mats][out][nb].  The zero-padded tail block of every row is
+ * encoded in full (all 128 codes are stored). */
+int hlwq_quantize(const void* w_bf16, int64_t n_mats, int64_t out, int64_t in,
+                  int block, int bits, void* packed_u8, void* norms_f16,
+                  void* hip_stream);
+
+/* Inverse of hlwq_quantize: unpack, centroid lookup, inverse rotation, scale
+ * by the fp16 norm, round to bf16; writes only the `in` real columns of every
+ * row of W_out [n_mats][out][in]. */
+int hlwq_dequantize(const void* packed_u8, const void* norms_f16, int64_t n_mats,
+                    int64_t out, int64_t in, int block, int bits,
+                    void* w_bf16_out, void* hip_stream);
+
+/* Quantize several matrices (e.g. the gate_up and down banks of a MoE layer,
+ * every expert of which is quantised independently: "Gemma-4-26B-A4B-it-HLWQ-Q5",
+ * "Technical Details") in one launch.  `mats` is a host array of n
+ * descriptors, read before the call returns; more than 16 descriptors are
+ * split over several launches.  bits = 5 or 3, block 128. */
+int hlwq_quantize_grouped(const hlwq_mat_desc* mats, int n, int bits, void* hip_stream);
+
+/* Inverse of hlwq_quantize_grouped over the same descriptors. */
+int hlwq_dequantize_grouped(const hlwq_mat_desc* mats, int n, int bits, void* hip_stream);
+
+/* Quantize a KV cache [batch][heads][tokens][head_dim] (bf16) per head
+ * vector: H256 rotation, 8 Lloyd-Max centroids, 3-bit codes ("Qwopus3.6-27B-v2
+ * · HLWQ Q5", "Methodology notes", KV bullet).  head_dim must be 256 and bits
+ * 3.  Tokens t < tokens - n_residual are encoded into packed
+ * [batch][heads][tq][96] and norms [batch][heads][tq]; the newest n_residual
+ * tokens (the unquantised residual window, 128 on that card) are not read. */
+int hlwq_kv_quantize(const void* kv_bf16, int64_t batch, int64_t heads, int64_t tokens,
+                     int head_dim, int bits, int64_t n_residual,
+                     void* packed_u8, void* norms_f16, void* hip_stream);
+
+/* Inverse of hlwq_kv_quantize: writes tokens t < tokens - n_residual of
+ * kv_out [batch][heads][tokens][head_dim]; the residual rows of kv_out are
+ * not touched (the caller keeps its bf16 residual tokens there). */
+int hlwq_kv_dequantize(const void* packed_u8, const void* norms_f16, int64_t batch,
+                       int64_t heads, int64_t tokens, int head_dim, int bits,
+                       int64_t n_residual, void* kv_bf16_out, void* hip_stream);
+
+/* Bytes of packed codes for `rows` rows of `in` columns: rows * nb * block * bits / 8.
+ * Returns 0 for invalid arguments. */
+size_t hlwq_packed_bytes(int64_t rows, int64_t in, int block, int bits);
+
+/* Number of fp16 norms for `rows` rows of `in` columns: rows * nb.  0 if invalid. */
+size_t hlwq_norm_count(int64_t rows, int64_t in, int block);
+
+/* Copy the fp32 codebook the kernels use: 2^bits centroids (ascending) and
+ * 2^bits - 1 decision thresholds.  bits = 5 or 3.  Host-only, no GPU needed. */
+int hlwq_centroids(int bits, float* centroids, float* thresholds);
+
+/* Copy the bucket table the kernels use to find a code with one compare:
+ * entries of {threshold bits (fp32, +inf if the bucket holds none), count of
+ * thresholds below the bucket}; a value y falls in entry
+ * (uint32_t) fmaf(y, 8, offset).  kind 0: Q5 weights (offset 96), 1: Q3
+ * weights (offset 96), 2: Q3 KV (offset 136).  Writes at most `capacity`
+ * pairs into `words` (2 * capacity uint32) and returns the entry count, or a
+ * negative status.  Host-only; exposed so the table can be verified. */
+int hlwq_search_table(int kind, uint32_t* words, int capacity, float* offset);
+
+/* Static, human-readable text for a status code. */
+const char* hlwq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HLWQ_H */

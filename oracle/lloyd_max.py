@@ -43,7 +43,7 @@ def _cell_mass(lo: np.ndarray, hi: np.ndarray) -> np.ndarray:
     return np.where(upper, ndtr(-lo) - ndtr(-hi), ndtr(hi) - ndtr(lo))
 
 
-def lloyd_max_gaussian(K: int, tol: float = 1e-13, max_iter: int = 200_000):
+def lloyd_max_gaussian(K: int, tol: float = 1e-15, max_iter: int = 200_000):
     """Return (centroids fp64 ascending, iterations) for K levels on N(0, 1)."""
     if K < 2:
         raise ValueError("K must be at least 2")

@@ -30,6 +30,8 @@ Trained weights are not available; these seeded tensors stand in for them.
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 CONFIG_IDS = {
@@ -117,14 +119,26 @@ def expert_matrix(config: str, tensor: str, expert: int, seed: int = DEFAULT_SEE
     return draw(dist, r, mat_shape, sigma, ofrac, omult)
 
 
-def weight(config: str, tensor: str, seed: int = DEFAULT_SEED) -> np.ndarray:
-    """A whole weight tensor as bf16 bits: [E, out, in] for banks, [out, in] otherwise."""
+def weight(config: str, tensor: str, seed: int = DEFAULT_SEED, workers: int = 8) -> np.ndarray:
+    """A whole weight tensor as bf16 bits: [E, out, in] for banks, [out, in] otherwise.
+
+    Experts are drawn on a thread pool (numpy's generators release the GIL);
+    each expert has its own stream, so the result does not depend on `workers`.
+    """
     tid, shape, dist, sigma, ofrac, omult = CONFIGS[config][tensor]
     if len(shape) == 2:
         return expert_matrix(config, tensor, 0, seed)
     out = np.empty(shape, dtype=np.uint16)
-    for e in range(shape[0]):
+
+    def fill(e):
         out[e] = expert_matrix(config, tensor, e, seed)
+
+    if workers > 1:
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(fill, range(shape[0])))
+    else:
+        for e in range(shape[0]):
+            fill(e)
     return out
 
 

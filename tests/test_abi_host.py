@@ -1,0 +1,141 @@
+"""Host-side checks of libhlwq (CPU only, no kernel is launched).
+
+The library must load without a GPU, export every function include/hlwq.h
+declares, carry exactly the oracle's codebook, and reject bad arguments with
+the documented status codes before touching a device.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import weight_quantization_amd as wq
+from oracle import hlwq_ref as ref
+from oracle import lloyd_max as lm
+
+OK, ENULL, ESHAPE, EBITS, EBLOCK, EDEV, EALIGN, ELIMIT = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return wq.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = wq.declared_functions()
+    assert len(names) == 11
+    raw = ctypes.CDLL(wq.binding.LIB_PATH)
+    for name in names:
+        assert hasattr(raw, name), name
+
+
+@pytest.mark.parametrize("bits", [5, 3])
+def test_codebook_matches_oracle(bits):
+    c, t = wq.hlwq_centroids(bits)
+    oc, ot = lm.table(bits)
+    assert np.array_equal(c.view(np.uint32), oc.view(np.uint32))
+    assert np.array_equal(t.view(np.uint32), ot.view(np.uint32))
+
+
+def _bucket_codes(table, offset, y):
+    # k = (uint32) fmaf(y, 8, offset): 8y + offset is exact in fp64 for fp32 y,
+    # so one rounding to fp32 reproduces the fused multiply-add.
+    u = (np.asarray(y, np.float32).astype(np.float64) * 8.0 + offset).astype(np.float32)
+    k = np.where(u > 0, np.trunc(u), 0).astype(np.int64)
+    thr = table[k, 0].view(np.float32)
+    return table[k, 1].astype(np.int64) + (np.asarray(y, np.float32) > thr)
+
+
+@pytest.mark.parametrize("kind,bits,limit", [(0, 5, 11.32), (1, 3, 11.32), (2, 3, 16.0)])
+def test_bucket_table_reproduces_threshold_count(kind, bits, limit):
+    # The kernels find codes with one table read and one compare; on every
+    # fp32 value near a threshold or a bucket edge, and on a dense sweep of the
+    # reachable range, that must equal the oracle's threshold count.
+    table, offset = wq.hlwq_search_table(kind)
+    _, b32 = lm.table(bits)
+    assert table.shape[0] * 1.0 > 8 * limit + offset
+    probes = np.concatenate([b32, (np.arange(table.shape[0] + 1) - offset) / 8.0]).astype(np.float32)
+    steps = np.arange(-2048, 2049, dtype=np.int64)
+    near = (probes.view(np.int32).astype(np.int64)[:, None] + steps[None, :])
+    pos = near[probes[:, None].repeat(steps.size, 1) >= 0]
+    y_near = np.concatenate([pos.astype(np.int32).view(np.float32),
+                             (-(pos.astype(np.int32).view(np.float32)))])
+    rng = np.random.default_rng(0)
+    y = np.concatenate([y_near, np.linspace(-limit, limit, 2_000_001, dtype=np.float32),
+                        rng.standard_normal(200_000).astype(np.float32), np.float32([0.0, -0.0])])
+    y = y[np.abs(y) <= limit]
+    assert np.array_equal(_bucket_codes(table, offset, y), ref.codes_from_y(y, b32))
+
+
+def test_size_helpers():
+    assert wq.hlwq_packed_bytes(64, 256, 128, 5) == 64 * 2 * 80
+    assert wq.hlwq_packed_bytes(2816 * 128, 704, 128, 5) == 2816 * 128 * 6 * 80
+    assert wq.hlwq_packed_bytes(10, 129, 128, 3) == 10 * 2 * 48
+    assert wq.hlwq_norm_count(2816, 704, 128) == 2816 * 6
+    assert wq.hlwq_packed_bytes(-1, 5, 128, 5) == 0
+    assert wq.hlwq_norm_count(1, -5, 128) == 0
+    assert wq.hlwq_packed_bytes(2 ** 62, 2 ** 40, 128, 5) == 0
+
+
+def test_status_strings(lib):
+    for st in (OK, ENULL, ESHAPE, EBITS, EBLOCK, EDEV, EALIGN, ELIMIT):
+        assert wq.hlwq_status_string(st) != "unknown status"
+    assert wq.hlwq_status_string(12345) == "unknown status"
+
+
+def test_quantize_argument_errors(lib):
+    q = lib.hlwq_quantize
+    A = 0x100000  # an aligned, never-dereferenced address
+    assert q(None, 1, 4, 128, 128, 5, A, A, None) == ENULL
+    assert q(A, 1, 4, 128, 128, 5, None, A, None) == ENULL
+    assert q(A, 1, 4, 128, 128, 4, A, A, None) == EBITS
+    assert q(A, 1, 4, 128, 64, 5, A, A, None) == EBLOCK
+    assert q(A, -1, 4, 128, 128, 5, A, A, None) == ESHAPE
+    assert q(A, 1, 4, -3, 128, 5, A, A, None) == ESHAPE
+    assert q(A, 2 ** 40, 2 ** 40, 128, 128, 5, A, A, None) == ESHAPE
+    assert q(A, 1, 4, 128, 128, 5, A + 8, A, None) == EALIGN
+    assert q(A, 1, 4, 128, 128, 5, A, A + 1, None) == EALIGN
+    assert q(A + 1, 1, 4, 128, 128, 5, A, A, None) == EALIGN
+    assert q(A, 1, 2 ** 31, 128 * 2, 128, 5, A, A, None) == ELIMIT
+    # zero-sized work is a no-op and accepts NULL
+    assert q(None, 0, 4, 128, 128, 5, None, None, None) == OK
+    assert q(None, 1, 0, 128, 128, 5, None, None, None) == OK
+    assert q(None, 1, 4, 0, 128, 5, None, None, None) == OK
+    d = lib.hlwq_dequantize
+    assert d(A, None, 1, 4, 128, 128, 5, A, None) == ENULL
+    assert d(A, A, 1, 4, 128, 128, 6, A, None) == EBITS
+    assert d(A, A, 1, 4, 128, 256, 5, A, None) == EBLOCK
+
+
+def test_grouped_argument_errors(lib):
+    A = 0x100000
+    descs = (wq.MatDesc * 3)()
+    descs[0] = wq.MatDesc(A, A, A, 4, 128)
+    descs[1] = wq.MatDesc(A, None, A, 4, 128)
+    descs[2] = wq.MatDesc(A, A, A, 4, 128)
+    assert lib.hlwq_quantize_grouped(descs, 3, 5, None) == ENULL
+    assert lib.hlwq_quantize_grouped(descs, -1, 5, None) == ESHAPE
+    assert lib.hlwq_quantize_grouped(None, 2, 5, None) == ENULL
+    assert lib.hlwq_quantize_grouped(None, 0, 5, None) == OK
+    assert lib.hlwq_dequantize_grouped(descs, 3, 2, None) == EBITS
+    descs[1] = wq.MatDesc(A, A, A, -4, 128)
+    assert lib.hlwq_dequantize_grouped(descs, 3, 5, None) == ESHAPE
+    empty = (wq.MatDesc * 2)()
+    empty[0] = wq.MatDesc(None, None, None, 0, 128)
+    empty[1] = wq.MatDesc(None, None, None, 7, 0)
+    assert lib.hlwq_quantize_grouped(empty, 2, 3, None) == OK
+
+
+def test_kv_argument_errors(lib):
+    A = 0x100000
+    kq, kd = lib.hlwq_kv_quantize, lib.hlwq_kv_dequantize
+    assert kq(A, 1, 4, 300, 128, 3, 128, A, A, None) == EBLOCK
+    assert kq(A, 1, 4, 300, 256, 5, 128, A, A, None) == EBITS
+    assert kq(A, 1, 4, -1, 256, 3, 128, A, A, None) == ESHAPE
+    assert kq(A, 1, 4, 300, 256, 3, -1, A, A, None) == ESHAPE
+    assert kq(None, 1, 4, 300, 256, 3, 128, A, A, None) == ENULL
+    assert kq(A, 1, 4, 300, 256, 3, 128, A + 4, A, None) == EALIGN
+    assert kd(A, A, 1, 4, 300, 256, 3, 128, A + 1, None) == EALIGN
+    # every token inside the residual window: nothing to do
+    assert kq(None, 1, 4, 128, 256, 3, 128, None, None, None) == OK
+    assert kd(None, None, 1, 4, 100, 256, 3, 128, None, None) == OK

@@ -1,0 +1,310 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle.
+
+Bar: packed codes, fp16 norms and bf16 dequantised weights bit-identical to the
+oracle's canonical fp32 tier on the same seeded inputs; against the fp64
+definition tier, code flips only within 1e-5 of a decision boundary (fraction
+< 1e-6) and dequantised weights within 1e-3 per unit of block norm.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import hlwq_ref as ref
+from oracle import lloyd_max as lm
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[gpu-parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def wq():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+    import weight_quantization_amd as m
+    m.load_library()
+    return m
+
+
+def to_dev(bits_u16: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(bits_u16).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def bf16_bits(t) -> np.ndarray:
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def f16_bits(t) -> np.ndarray:
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def check_matrix(wq, w_bits: np.ndarray, bits: int, label: str):
+    """Quantize + dequantize one [rows, in] matrix on the GPU and compare bit for bit."""
+    rows, n_in = w_bits.shape
+    _say(label, "rows", rows, "in", n_in, "bits", bits)
+    w = to_dev(w_bits)
+    packed, norms = wq.hlwq_quantize(w, bits)
+    out = wq.hlwq_dequantize(packed, norms, n_in, bits)
+    torch.cuda.synchronize()
+    op, on = ref.quantize_c(w_bits, bits)
+    gp = packed.cpu().numpy()
+    gn = f16_bits(norms)
+    assert np.array_equal(gn, on.view(np.uint16)), f"{label}: fp16 norms differ"
+    assert np.array_equal(gp, op), f"{label}: packed codes differ"
+    od = ref.dequantize_c(op, on, n_in, bits)
+    assert np.array_equal(bf16_bits(out), od), f"{label}: dequantised bf16 differs"
+
+
+def test_linear_64x256_q5_matches_oracle_and_golden(wq):
+    import json
+    import os
+    w_bits = synth.weight("linear_64x256", "W")
+    check_matrix(wq, w_bits, 5, "linear_64x256")
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "linear_64x256_q5.json")))
+    packed, norms = wq.hlwq_quantize(to_dev(w_bits), 5)
+    assert bytes(packed.cpu().numpy().ravel()).hex() == g["packed_hex"]
+
+
+@pytest.mark.parametrize("bits", [5, 3])
+@pytest.mark.parametrize("n_in", [1, 7, 8, 64, 120, 127, 128, 129, 200, 256, 704, 1000])
+def test_shapes_and_tails(wq, bits, n_in):
+    rows = 300 if n_in <= 256 else 97
+    w = synth.random_bf16((rows, n_in), seed=n_in, key=bits)
+    check_matrix(wq, w, bits, f"shape-{n_in}")
+
+
+@pytest.mark.parametrize("bits", [5, 3])
+def test_many_tiles_with_outliers(wq, bits):
+    w = synth.random_bf16((3001, 384), seed=5, outlier_frac=0.001, outlier_mult=20.0)
+    check_matrix(wq, w, bits, "tiles-outliers")
+    w = synth.random_bf16((257, 1536), seed=6, dist="student_t5")
+    check_matrix(wq, w, bits, "tiles-t5")
+
+
+def test_unaligned_rows(wq):
+    # rows starting at odd element offsets take the element-wise path
+    for n_in in (129, 255, 704):
+        w_bits = synth.random_bf16((41, n_in), seed=n_in)
+        base = torch.zeros(41 * n_in + 1, dtype=torch.bfloat16, device="cuda")
+        base[1:] = to_dev(w_bits).reshape(-1)
+        w = base[1:].view(41, n_in)
+        assert w.data_ptr() % 16 != 0
+        packed, norms = wq.hlwq_quantize(w, 5)
+        outbuf = torch.zeros(41 * n_in + 1, dtype=torch.bfloat16, device="cuda")
+        out = outbuf[1:].view(41, n_in)
+        wq.hlwq_dequantize(packed, norms, n_in, 5, out=out)
+        op, on = ref.quantize_c(w_bits, 5)
+        assert np.array_equal(packed.cpu().numpy(), op)
+        assert np.array_equal(f16_bits(norms), on.view(np.uint16))
+        assert np.array_equal(bf16_bits(out), ref.dequantize_c(op, on, n_in, 5))
+        assert bf16_bits(outbuf[:1])[0] == 0
+
+
+def _special_rows():
+    f = synth.f32_to_bf16_bits
+    rows = []
+    z = np.zeros(256, np.float32)
+    rows.append(z.copy())                                   # zero blocks
+    oh = z.copy(); oh[37] = 0.03125; oh[128 + 5] = -3.0     # one-hot blocks
+    rows.append(oh)
+    rows.append(np.full(256, 0.015625, np.float32))         # constant
+    rows.append(np.full(256, -7.5, np.float32))
+    rng = np.random.default_rng(3)
+    rows.append((rng.standard_normal(256) * 1e-30).astype(np.float32))   # squares underflow
+    rows.append((rng.standard_normal(256) * 1e-20).astype(np.float32))
+    rows.append((rng.standard_normal(256) * 1e15).astype(np.float32))    # large but finite squares
+    mixed = (rng.standard_normal(256) * np.exp(rng.uniform(-40, 20, 256))).astype(np.float32)
+    rows.append(mixed)
+    neg0 = z.copy(); neg0[::2] = -0.0; neg0[7] = 1.0
+    rows.append(neg0)
+    alt = np.where(np.arange(256) % 2 == 0, 1.0, -1.0).astype(np.float32)
+    rows.append(alt)
+    return f(np.stack(rows))
+
+
+@pytest.mark.parametrize("bits", [5, 3])
+def test_special_blocks(wq, bits):
+    w = _special_rows()
+    w[8, ::2] = 0x8000  # keep the negative zeros (rounding maps -0.0 to 0x8000 already)
+    check_matrix(wq, w, bits, "special")
+
+
+def test_grouped_launch_splits(wq):
+    # 20 matrices of mixed shapes: two launches of up to 16 descriptors
+    rng = np.random.default_rng(8)
+    items, host = [], []
+    for i in range(20):
+        rows = int(rng.integers(1, 300))
+        n_in = int(rng.choice([64, 128, 200, 512, 704]))
+        wb = synth.random_bf16((rows, n_in), seed=100 + i)
+        w = to_dev(wb)
+        nb = -(-n_in // 128)
+        p = torch.empty((rows, nb, 80), dtype=torch.uint8, device="cuda")
+        n = torch.empty((rows, nb), dtype=torch.float16, device="cuda")
+        items.append((w, p, n))
+        host.append(wb)
+    _say("grouped quantize, 20 matrices")
+    wq.hlwq_quantize_grouped(items, 5)
+    outs = [(torch.empty_like(w), p, n) for (w, p, n) in items]
+    wq.hlwq_dequantize_grouped(outs, 5)
+    torch.cuda.synchronize()
+    for (w, p, n), (o, _, _), wb in zip(items, outs, host):
+        op, on = ref.quantize_c(wb, 5)
+        assert np.array_equal(p.cpu().numpy(), op)
+        assert np.array_equal(f16_bits(n), on.view(np.uint16))
+        assert np.array_equal(bf16_bits(o), ref.dequantize_c(op, on, wb.shape[1], 5))
+
+
+def test_non_default_stream_and_determinism(wq):
+    wb = synth.random_bf16((512, 2048), seed=12)
+    w = to_dev(wb)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        p1, n1 = wq.hlwq_quantize(w, 5)
+    s.synchronize()
+    p2, n2 = wq.hlwq_quantize(w, 5)
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p2) and torch.equal(n1, n2)
+    op, on = ref.quantize_c(wb, 5)
+    assert np.array_equal(p1.cpu().numpy(), op)
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 300), (2, 3, 1000), (1, 1, 129), (1, 4, 128), (1, 1, 5)])
+def test_kv_cache_small(wq, shape):
+    B, H, T = shape
+    kv = synth.random_bf16((B, H, T, 256), seed=T, sigma=1.0)
+    _say("kv", shape)
+    dev = to_dev(kv)
+    packed, norms = wq.hlwq_kv_quantize(dev, n_residual=128)
+    out = to_dev(np.full((B, H, T, 256), 0x3F80, np.uint16))  # 1.0 sentinel
+    wq.hlwq_kv_dequantize(packed, norms, out, n_residual=128)
+    torch.cuda.synchronize()
+    op, on = ref.kv_quantize_c(kv, n_residual=128)
+    assert np.array_equal(packed.cpu().numpy(), op)
+    assert np.array_equal(f16_bits(norms), on.view(np.uint16))
+    tq = max(T - 128, 0)
+    got = bf16_bits(out)
+    assert np.array_equal(got[:, :, :tq], ref.kv_dequantize_c(op, on))
+    assert np.all(got[:, :, tq:] == 0x3F80), "residual window must stay untouched"
+
+
+# --------------------------------------------------------------------------
+# full-size workloads, launched as the benchmark launches them; sampled outputs
+# --------------------------------------------------------------------------
+
+def _bank_check(wq, config, bits, samples):
+    tensors = list(synth.CONFIGS[config])
+    host = {t: synth.weight(config, t) for t in tensors}
+    _say(config, "generated", {t: host[t].shape for t in tensors})
+    items, outs = [], []
+    for t in tensors:
+        w = to_dev(host[t])
+        E, rows, n_in = host[t].shape
+        nb = -(-n_in // 128)
+        p = torch.empty((E, rows, nb, 16 * bits), dtype=torch.uint8, device="cuda")
+        n = torch.empty((E, rows, nb), dtype=torch.float16, device="cuda")
+        items.append((w, p, n))
+    wq.hlwq_quantize_grouped(items, bits)
+    for (w, p, n) in items:
+        outs.append((torch.empty_like(w), p, n))
+    wq.hlwq_dequantize_grouped(outs, bits)
+    torch.cuda.synchronize()
+    _say(config, "gpu done")
+    for t, (w, p, n), (o, _, _) in zip(tensors, items, outs):
+        for e in samples:
+            wb = host[t][e]
+            op, on = ref.quantize_c(wb, bits)
+            assert np.array_equal(p[e].cpu().numpy(), op), (config, t, e)
+            assert np.array_equal(f16_bits(n[e]), on.view(np.uint16)), (config, t, e)
+            assert np.array_equal(bf16_bits(o[e]), ref.dequantize_c(op, on, wb.shape[1], bits)), (config, t, e)
+        # property over the whole bank: every code byte stream decodes to in-range
+        # codes and every norm is finite and positive
+        assert torch.isfinite(n.float()).all() and (n.float() > 0).all()
+    del items, outs
+    torch.cuda.empty_cache()
+
+
+def test_qwen36_moe_bank_full(wq):
+    _bank_check(wq, "qwen36_moe_bank", 5, samples=(0, 137, 255))
+
+
+def test_gemma4_moe_bank_full(wq):
+    _bank_check(wq, "gemma4_moe_bank", 5, samples=(0, 63, 127))
+
+
+@pytest.mark.parametrize("bits", [5, 3])
+def test_dense_5120_full_sampled_rows(wq, bits):
+    rng = np.random.default_rng(bits)
+    for t in synth.CONFIGS["dense_5120"]:
+        wb = synth.weight("dense_5120", t)
+        _say("dense_5120", t, wb.shape, "bits", bits)
+        w = to_dev(wb)
+        packed, norms = wq.hlwq_quantize(w, bits)
+        out = wq.hlwq_dequantize(packed, norms, wb.shape[1], bits)
+        torch.cuda.synchronize()
+        rows = np.sort(rng.choice(wb.shape[0], 96, replace=False))
+        idx = torch.from_numpy(rows).cuda()
+        op, on = ref.quantize_c(wb[rows], bits)
+        assert np.array_equal(packed[idx].cpu().numpy(), op)
+        assert np.array_equal(f16_bits(norms[idx]), on.view(np.uint16))
+        assert np.array_equal(bf16_bits(out[idx]), ref.dequantize_c(op, on, wb.shape[1], bits))
+        del w, packed, norms, out
+
+
+def test_kv_h256_full(wq):
+    for t in ("K", "V"):
+        kv = synth.kv_cache("kv_h256", t)
+        _say("kv_h256", t, kv.shape)
+        dev = to_dev(kv)
+        packed, norms = wq.hlwq_kv_quantize(dev, n_residual=128)
+        out = torch.empty_like(dev)
+        out[:, :, -128:] = dev[:, :, -128:]
+        wq.hlwq_kv_dequantize(packed, norms, out, n_residual=128)
+        torch.cuda.synchronize()
+        assert torch.equal(out[:, :, -128:], dev[:, :, -128:])
+        for h, t0 in ((0, 0), (1, 12345), (3, 32640 - 512)):
+            sl = kv[:, h:h + 1, t0:t0 + 512]
+            op, on = ref.kv_quantize_c(np.concatenate([sl, np.zeros((1, 1, 128, 256), np.uint16)], axis=2),
+                                       n_residual=128)
+            assert np.array_equal(packed[:, h:h + 1, t0:t0 + 512].cpu().numpy(), op)
+            assert np.array_equal(f16_bits(norms[:, h:h + 1, t0:t0 + 512]), on.view(np.uint16))
+            assert np.array_equal(bf16_bits(out[:, h:h + 1, t0:t0 + 512]), ref.kv_dequantize_c(op, on))
+
+
+# --------------------------------------------------------------------------
+# tolerances against the fp64 definition tier
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [5, 3])
+def test_definition_tier_tolerances(wq, bits):
+    wb = np.concatenate([synth.expert_matrix("qwen36_moe_bank", "gate_up", e) for e in range(4)])  # 8.4M weights
+    w = to_dev(wb)
+    packed, norms = wq.hlwq_quantize(w, bits)
+    out = wq.hlwq_dequantize(packed, norms, 2048, bits)
+    torch.cuda.synchronize()
+    c32, _ = lm.table(bits)
+    x, _ = ref.blocks_from_rows(wb)
+    codes_d, n_d, y_d = ref.quantize_def(x, bits, c32)
+    codes_g = ref.unpack_codes(packed.cpu().numpy(), bits)
+    flips = codes_g != codes_d
+    dist = ref.boundary_distance(y_d[flips], c32)
+    _say(f"bits={bits}: code flips vs fp64 definition: {int(flips.sum())} of {flips.size} "
+         f"({flips.mean():.2e}); max boundary distance {dist.max() if dist.size else 0:.2e}")
+    assert np.all(dist < 1e-5)
+    assert flips.mean() < 1e-6
+    ghat = ref.bf16_to_f32(bf16_bits(out)).astype(np.float64).reshape(x.shape)
+    dd = ref.dequantize_def(codes_g, f16_bits(norms).view(np.float16).astype(np.float64), bits, c32)
+    # within one bf16 ulp of the exact inverse everywhere ...
+    assert np.all(np.abs(ghat - dd) <= 2.0 ** -8 * np.abs(dd) + 1e-7 * n_d[..., None])
+    # ... and within 1e-3 per unit of block norm of the bf16-rounded exact inverse,
+    # except where fp32 rounding moved a value across a bf16 rounding boundary
+    dd_bf16 = ref.bf16_to_f32(ref.f32_to_bf16_rne(dd.astype(np.float32))).astype(np.float64)
+    far = np.abs(ghat - dd_bf16) > 1e-3 * n_d[..., None]
+    _say(f"bits={bits}: dequant beyond 1e-3*n of the rounded fp64 inverse: {int(far.sum())} ({far.mean():.2e})")
+    assert far.mean() < 1e-5

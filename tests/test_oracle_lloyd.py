@@ -132,3 +132,17 @@ def test_threshold_count_is_nearest_centroid(bits):
     want = np.array(want)
     assert np.array_equal(ref.codes_from_y(y, b32), want)
     assert np.array_equal(ref.nearest_code(y, c32), want)
+
+
+@pytest.mark.parametrize("K", [4, 8, 32])
+def test_fp32_table_is_unambiguous(K):
+    # The fp64 fixed point sits far (> 1e-10) from every fp32 rounding
+    # boundary, so any converged Lloyd implementation rounds to the same fp32
+    # table; the residual iteration error is below 1e-12.
+    c, _ = lm.lloyd_max_gaussian(K)
+    c32 = c.astype(np.float32)
+    up = np.nextafter(c32, np.float32(np.inf)).astype(np.float64)
+    dn = np.nextafter(c32, np.float32(-np.inf)).astype(np.float64)
+    mid_up = 0.5 * (c32.astype(np.float64) + up)
+    mid_dn = 0.5 * (c32.astype(np.float64) + dn)
+    assert np.min(np.minimum(np.abs(c - mid_up), np.abs(c - mid_dn))) > 1e-10

@@ -1,0 +1,286 @@
+"""ctypes binding of libhlwq (declared in include/hlwq.h).
+
+Argument marshalling only: every function below checks the torch tensors it
+is given, passes their device pointers, sizes and the current HIP stream to the
+C function of the same name, and raises on a non-zero status.  All compute runs
+in the HIP kernels of libhlwq.so; there is no fallback of any kind.  torch is
+used for device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhlwq.so")
+HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "hlwq.h")
+
+HLWQ_OK = 0
+BLOCK = 128
+KV_DIM = 256
+
+
+class HLWQError(RuntimeError):
+    def __init__(self, func: str, status: int, text: str):
+        super().__init__(f"{func} failed: {text} (status {status})")
+        self.status = status
+
+
+class MatDesc(ctypes.Structure):
+    _fields_ = [
+        ("w", ctypes.c_void_p),
+        ("packed", ctypes.c_void_p),
+        ("norms", ctypes.c_void_p),
+        ("rows", ctypes.c_int64),
+        ("in_", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_vp = ctypes.c_void_p
+
+_SIGNATURES = {
+    "hlwq_quantize": (_int, [_vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp]),
+    "hlwq_dequantize": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp]),
+    "hlwq_quantize_grouped": (_int, [ctypes.POINTER(MatDesc), _int, _int, _vp]),
+    "hlwq_dequantize_grouped": (_int, [ctypes.POINTER(MatDesc), _int, _int, _vp]),
+    "hlwq_kv_quantize": (_int, [_vp, _i64, _i64, _i64, _int, _int, _i64, _vp, _vp, _vp]),
+    "hlwq_kv_dequantize": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _i64, _vp, _vp]),
+    "hlwq_packed_bytes": (ctypes.c_size_t, [_i64, _i64, _int, _int]),
+    "hlwq_norm_count": (ctypes.c_size_t, [_i64, _i64, _int]),
+    "hlwq_search_table": (_int, [_int, ctypes.POINTER(ctypes.c_uint32), _int, ctypes.POINTER(ctypes.c_float)]),
+    "hlwq_status_string": (ctypes.c_char_p, [_int]),
+}
+_SIGNATURES["hlwq_centroids"] = (_int, [_int, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)])
+
+
+def declared_functions(header: str = HEADER_PATH) -> list[str]:
+    """Names of the functions include/hlwq.h declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hlwq_[a-z_0-9]+)\s*\(", text)))
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libhlwq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m weight_quantization_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(func: str, status: int):
+    if status != HLWQ_OK:
+        raise HLWQError(func, status, hlwq_status_string(status))
+
+
+# --------------------------------------------------------------------------
+# host-only helpers
+# --------------------------------------------------------------------------
+
+def hlwq_status_string(status: int) -> str:
+    return load_library().hlwq_status_string(int(status)).decode()
+
+
+def hlwq_packed_bytes(rows: int, n_in: int, block: int = BLOCK, bits: int = 5) -> int:
+    return int(load_library().hlwq_packed_bytes(rows, n_in, block, bits))
+
+
+def hlwq_norm_count(rows: int, n_in: int, block: int = BLOCK) -> int:
+    return int(load_library().hlwq_norm_count(rows, n_in, block))
+
+
+def hlwq_centroids(bits: int):
+    """(centroids float32[2^bits], thresholds float32[2^bits - 1]) used by the kernels."""
+    K = 1 << bits
+    c = (ctypes.c_float * K)()
+    t = (ctypes.c_float * max(K - 1, 1))()
+    _check("hlwq_centroids", load_library().hlwq_centroids(bits, c, t))
+    return np.frombuffer(c, dtype=np.float32).copy(), np.frombuffer(t, dtype=np.float32)[:K - 1].copy()
+
+
+def hlwq_search_table(kind: int):
+    """(entries uint32[n, 2] = {threshold bits, base}, offset) of a bucket table."""
+    lib = load_library()
+    off = ctypes.c_float()
+    n = lib.hlwq_search_table(kind, None, 0, ctypes.byref(off))
+    if n < 0:
+        _check("hlwq_search_table", n)
+    buf = (ctypes.c_uint32 * (2 * n))()
+    lib.hlwq_search_table(kind, buf, n, ctypes.byref(off))
+    return np.frombuffer(buf, dtype=np.uint32).reshape(n, 2).copy(), float(off.value)
+
+
+# --------------------------------------------------------------------------
+# device calls (torch tensors in device memory)
+# --------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _ptr(t) -> int:
+    return int(t.data_ptr()) if t is not None and t.numel() > 0 else 0
+
+
+def _need(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be in device memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def packed_shape(w_shape, bits: int):
+    *lead, n_in = w_shape
+    nb = -(-n_in // BLOCK)
+    return (*lead, nb, 16 * bits), (*lead, nb)
+
+
+def hlwq_quantize(w, bits: int = 5, packed=None, norms=None, stream=None):
+    """Quantize a bf16 [out, in] or [n_mats, out, in] tensor; returns (packed u8, norms fp16)."""
+    torch = _torch()
+    _need(w, torch.bfloat16, "w")
+    if w.dim() not in (2, 3):
+        raise ValueError("w must be [out, in] or [n_mats, out, in]")
+    n_mats, out, n_in = (1, *w.shape) if w.dim() == 2 else tuple(w.shape)
+    pshape, nshape = packed_shape(tuple(w.shape), bits)
+    if packed is None:
+        packed = torch.empty(pshape, dtype=torch.uint8, device=w.device)
+    if norms is None:
+        norms = torch.empty(nshape, dtype=torch.float16, device=w.device)
+    _need(packed, torch.uint8, "packed")
+    _need(norms, torch.float16, "norms")
+    if tuple(packed.shape) != pshape or tuple(norms.shape) != nshape:
+        raise ValueError("packed / norms shape mismatch")
+    st = load_library().hlwq_quantize(_ptr(w), n_mats, out, n_in, BLOCK, bits, _ptr(packed), _ptr(norms),
+                                      _stream_handle(stream))
+    _check("hlwq_quantize", st)
+    return packed, norms
+
+
+def hlwq_dequantize(packed, norms, n_in: int, bits: int = 5, out=None, stream=None):
+    """Inverse of hlwq_quantize; returns bf16 [.., out, in]."""
+    torch = _torch()
+    _need(packed, torch.uint8, "packed")
+    _need(norms, torch.float16, "norms")
+    if packed.dim() not in (3, 4) or packed.shape[-1] != 16 * bits:
+        raise ValueError("packed must be [.., out, nb, 16*bits]")
+    lead = tuple(packed.shape[:-2])
+    nb = packed.shape[-2]
+    if nb != -(-n_in // BLOCK) or tuple(norms.shape) != lead + (nb,):
+        raise ValueError("packed / norms / in mismatch")
+    n_mats, rows = (1, lead[0]) if len(lead) == 1 else lead
+    if out is None:
+        out = torch.empty(lead + (n_in,), dtype=torch.bfloat16, device=packed.device)
+    _need(out, torch.bfloat16, "out")
+    if tuple(out.shape) != lead + (n_in,):
+        raise ValueError("out shape mismatch")
+    st = load_library().hlwq_dequantize(_ptr(packed), _ptr(norms), n_mats, rows, n_in, BLOCK, bits, _ptr(out),
+                                        _stream_handle(stream))
+    _check("hlwq_dequantize", st)
+    return out
+
+
+def _descs(items):
+    arr = (MatDesc * max(len(items), 1))()
+    for i, (w, p, n) in enumerate(items):
+        n_in = w.shape[-1]
+        rows = w.numel() // n_in if n_in else 0
+        arr[i] = MatDesc(_ptr(w), _ptr(p), _ptr(n), rows, n_in)
+    return arr
+
+
+def hlwq_quantize_grouped(items, bits: int = 5, stream=None):
+    """items: list of (w bf16, packed u8, norms fp16) triples, all preallocated."""
+    torch = _torch()
+    for w, p, n in items:
+        _need(w, torch.bfloat16, "w")
+        _need(p, torch.uint8, "packed")
+        _need(n, torch.float16, "norms")
+        ps, ns = packed_shape(tuple(w.shape), bits)
+        if tuple(p.shape) != ps or tuple(n.shape) != ns:
+            raise ValueError("packed / norms shape mismatch")
+    arr = _descs(items)
+    st = load_library().hlwq_quantize_grouped(arr, len(items), bits, _stream_handle(stream))
+    _check("hlwq_quantize_grouped", st)
+
+
+def hlwq_dequantize_grouped(items, bits: int = 5, stream=None):
+    """items: list of (w_out bf16, packed u8, norms fp16) triples, all preallocated."""
+    torch = _torch()
+    for w, p, n in items:
+        _need(w, torch.bfloat16, "w")
+        _need(p, torch.uint8, "packed")
+        _need(n, torch.float16, "norms")
+        ps, ns = packed_shape(tuple(w.shape), bits)
+        if tuple(p.shape) != ps or tuple(n.shape) != ns:
+            raise ValueError("packed / norms shape mismatch")
+    arr = _descs(items)
+    st = load_library().hlwq_dequantize_grouped(arr, len(items), bits, _stream_handle(stream))
+    _check("hlwq_dequantize_grouped", st)
+
+
+def hlwq_kv_quantize(kv, n_residual: int = 128, bits: int = 3, packed=None, norms=None, stream=None):
+    """Quantize a bf16 KV cache [B, H, T, 256]; returns (packed [B,H,Tq,96], norms [B,H,Tq])."""
+    torch = _torch()
+    _need(kv, torch.bfloat16, "kv")
+    if kv.dim() != 4:
+        raise ValueError("kv must be [batch, heads, tokens, head_dim]")
+    B, H, T, D = kv.shape
+    tq = max(T - n_residual, 0)
+    if packed is None:
+        packed = torch.empty((B, H, tq, D * bits // 8), dtype=torch.uint8, device=kv.device)
+    if norms is None:
+        norms = torch.empty((B, H, tq), dtype=torch.float16, device=kv.device)
+    _need(packed, torch.uint8, "packed")
+    _need(norms, torch.float16, "norms")
+    if tuple(packed.shape) != (B, H, tq, D * bits // 8) or tuple(norms.shape) != (B, H, tq):
+        raise ValueError("packed / norms shape mismatch")
+    st = load_library().hlwq_kv_quantize(_ptr(kv), B, H, T, D, bits, n_residual, _ptr(packed), _ptr(norms),
+                                         _stream_handle(stream))
+    _check("hlwq_kv_quantize", st)
+    return packed, norms
+
+
+def hlwq_kv_dequantize(packed, norms, kv_out, n_residual: int = 128, bits: int = 3, stream=None):
+    """Write tokens t < T - n_residual of kv_out [B, H, T, 256] from packed / norms."""
+    torch = _torch()
+    _need(packed, torch.uint8, "packed")
+    _need(norms, torch.float16, "norms")
+    _need(kv_out, torch.bfloat16, "kv_out")
+    B, H, T, D = kv_out.shape
+    tq = max(T - n_residual, 0)
+    if tuple(packed.shape) != (B, H, tq, D * bits // 8) or tuple(norms.shape) != (B, H, tq):
+        raise ValueError("packed / norms shape mismatch")
+    st = load_library().hlwq_kv_dequantize(_ptr(packed), _ptr(norms), B, H, T, D, bits, n_residual, _ptr(kv_out),
+                                           _stream_handle(stream))
+    _check("hlwq_kv_dequantize", st)
+    return kv_out
