@@ -118,8 +118,8 @@ def _special_rows():
     rng = np.random.default_rng(3)
     rows.append((rng.standard_normal(256) * 1e-30).astype(np.float32))   # squares underflow
     rows.append((rng.standard_normal(256) * 1e-20).astype(np.float32))
-    rows.append((rng.standard_normal(256) * 1e15).astype(np.float32))    # large but finite squares
-    mixed = (rng.standard_normal(256) * np.exp(rng.uniform(-40, 20, 256))).astype(np.float32)
+    rows.append((rng.standard_normal(256) * 2e3).astype(np.float32))     # norm near the fp16 limit
+    mixed = (rng.standard_normal(256) * np.exp(rng.uniform(-40, 5, 256))).astype(np.float32)
     rows.append(mixed)
     neg0 = z.copy(); neg0[::2] = -0.0; neg0[7] = 1.0
     rows.append(neg0)
