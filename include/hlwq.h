@@ -52,9 +52,10 @@
  * Inputs must be finite; a block whose squared norm overflows fp32 (an entry
  * above ~1.8e19 in magnitude) yields an infinite norm and unspecified codes.
  *
- * Alignment: `packed` must be 16-byte aligned, `norms` and bf16 buffers 2-byte
- * aligned; W rows need no further alignment (rows whose start is not 16-byte
- * aligned take a slower element-wise path).
+ * Alignment: `packed` and KV-cache buffers must be 16-byte aligned, `norms`
+ * and weight buffers 2-byte aligned.  Weight matrices whose rows do not all
+ * start 16-byte aligned (in % 8 != 0, or an unaligned W) are handled, on a
+ * slower element-wise path.
  */
 #ifndef HLWQ_H
 #define HLWQ_H

@@ -136,6 +136,8 @@ def test_kv_argument_errors(lib):
     assert kq(None, 1, 4, 300, 256, 3, 128, A, A, None) == ENULL
     assert kq(A, 1, 4, 300, 256, 3, 128, A + 4, A, None) == EALIGN
     assert kd(A, A, 1, 4, 300, 256, 3, 128, A + 1, None) == EALIGN
+    assert kq(A + 2, 1, 4, 300, 256, 3, 128, A, A, None) == EALIGN
+    assert kq(A, 1, 4, 300, 256, 3, 128, A, A + 1, None) == EALIGN
     # every token inside the residual window: nothing to do
     assert kq(None, 1, 4, 128, 256, 3, 128, None, None, None) == OK
     assert kd(None, None, 1, 4, 100, 256, 3, 128, None, None) == OK

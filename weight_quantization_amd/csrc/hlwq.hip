@@ -28,6 +28,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cfloat>
 #include <cstdint>
 #include <cstring>
@@ -65,15 +66,15 @@ const uint32_t h_kvsearch3[2 * HLWQ_KV_SEARCH_ENTRIES] = HLWQ_KV_SEARCH_3;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (finite values; the kernels only
-// produce finite values for finite inputs).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
+// two fp32 -> packed bf16 pair (v_cvt_pk_bf16_f32: round to nearest even).
+// Dequantised values are never fp32 denormals (|value| >= 2^-59 when nonzero:
+// centroid sums are multiples of 2^-27 and the scale is at least 2^-32), so
+// the conversion agrees with bf16_rne bit for bit.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // fp32 -> fp16 bits (round to nearest even, overflow to inf) and back (exact)
@@ -83,6 +84,21 @@ __device__ __forceinline__ float f16_value(uint16_t b) { return static_cast<floa
 // value of the lane whose id differs in bit 0 (quad permutation [1,0,3,2])
 __device__ __forceinline__ float lane_xor1(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+
+// Butterfly across a lane pair: the even lane holds a, the odd lane b; both
+// call this with sgn = +1 (even) or -1 (odd) and get a + b, resp. a - b.
+// partner + sgn * self is that sum with one rounding (sgn * self is exact),
+// and the partner operand folds into a DPP-modified add.
+__device__ __forceinline__ float cross_pair(float self, float sgn) { return lane_xor1(self) + self * sgn; }
+
+// +1 on even lanes, -1 on odd lanes; laundered through an empty asm so the
+// compiler keeps "self * sgn" as a multiply (rewriting it into a select of
+// two butterflies would stop the DPP operand from folding into the add)
+__device__ __forceinline__ float pair_sign(uint32_t half) {
+  float s = half ? -1.0f : 1.0f;
+  asm volatile("" : "+v"(s));
+  return s;
 }
 
 // Unpack 8 bf16 from a 16-byte word into x[8*c .. 8*c+7].
@@ -120,26 +136,22 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ p, int n
   }
 }
 
-// Store 128 values as bf16 to p, only the first n (1..128).
-__device__ __forceinline__ void store_block(uint16_t* __restrict__ p, int n, const float (&w)[kBlock]) {
+// Store the first n (1..128) values of a block, packed as bf16 pairs, to p.
+__device__ __forceinline__ void store_block(uint16_t* __restrict__ p, int n, const uint32_t (&pk)[kBlock / 2]) {
   const bool vec_ok = ((reinterpret_cast<uintptr_t>(p) & 15u) == 0);
   if (vec_ok && (n & 7) == 0) {
     u32x4* q = reinterpret_cast<u32x4*>(p);
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
       if (8 * c < n) {
-        u32x4 v;
-        v.x = pack_bf16x2(w[8 * c + 0], w[8 * c + 1]);
-        v.y = pack_bf16x2(w[8 * c + 2], w[8 * c + 3]);
-        v.z = pack_bf16x2(w[8 * c + 4], w[8 * c + 5]);
-        v.w = pack_bf16x2(w[8 * c + 6], w[8 * c + 7]);
+        const u32x4 v = {pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]};
         __builtin_nontemporal_store(v, q + c);
       }
     }
   } else {
 #pragma unroll
     for (int j = 0; j < kBlock; ++j)
-      if (j < n) p[j] = static_cast<uint16_t>(bf16_rne(w[j]));
+      if (j < n) p[j] = static_cast<uint16_t>(pk[j / 2] >> (16 * (j & 1)));
   }
 }
 
@@ -217,100 +229,241 @@ __device__ __forceinline__ void decode(const uint32_t (&w)[L * BITS / 32], const
 }
 
 // ---------------------------------------------------------------------------
+// LDS staging
+//
+// Every wave owns a 16 KB slice of LDS.  Inputs reach it through direct
+// global->LDS loads (global_load_lds_dwordx4): in load instruction i, lane l
+// fills slot 64 i + l, so each instruction is one contiguous 1 KB of LDS and,
+// with the slot->chunk map below, one contiguous 1 KB of global memory too.
+// The map XORs the low 4 bits of a 16-byte chunk index with its 256-byte-row
+// index: when every lane then reads chunk c of its own 256-byte block, 16
+// consecutive lanes touch 16 different bank groups.  Outputs go the other
+// way: lanes write their results into the slice, the wave reads it back in
+// chunk order and issues 1 KB-contiguous global stores.  The slice is private
+// to the wave and LDS operations of one wave complete in order, so no
+// workgroup barrier is needed.
+// ---------------------------------------------------------------------------
+
+constexpr int kWaves = kThreads / 64;  // waves per workgroup
+constexpr int kStage = 16384;          // LDS bytes per wave
+
+__device__ __forceinline__ uint32_t swz(uint32_t q) { return q ^ ((q >> 4) & 15u); }
+
+// wait for this wave's outstanding vector-memory operations, including the
+// direct-to-LDS loads; the memory clobber keeps LDS reads below it
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Stage `bytes` (<= 1024 * NI) of global memory starting at the 16-byte
+// aligned address src: chunk q (16 bytes) lands in slot swz(q) if SWZ, else q.
+// Chunks past `bytes` re-read src and are never consumed.
+template <int NI, bool SWZ>
+__device__ __forceinline__ void stage_in(const uint8_t* src, uint32_t bytes, uint8_t* stage, int lane) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint32_t slot = 64u * i + lane;
+    const uint32_t q = SWZ ? swz(slot) : slot;
+    const uint8_t* a = (16u * q < bytes) ? src + 16u * q : src;
+    __builtin_amdgcn_global_load_lds(a, stage + 1024 * i, 16, 0, 0);
+  }
+}
+
+// Write back `bytes` of staged output (chunk q in slot swz(q) if SWZ) to dst
+// with 1 KB-contiguous stores.
+template <int NI, bool SWZ>
+__device__ __forceinline__ void stage_out(uint8_t* dst, uint32_t bytes, const uint8_t* stage, int lane) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint32_t q = 64u * i + lane;
+    if (16u * q < bytes) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + 16u * (SWZ ? swz(q) : q));
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + 16u * q));
+    }
+  }
+}
+
+__device__ __forceinline__ int64_t first_lane64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Read one 128-value block whose bytes start at byte offset `off` (a multiple
+// of 16) of a swizzled stage; only the first n values are real.
+__device__ __forceinline__ void read_staged_block(const uint8_t* stage, uint32_t off, int n, float (&x)[kBlock]) {
+  const uint32_t q0 = off >> 4;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (8 * c < n) v = *reinterpret_cast<const u32x4*>(stage + 16u * swz(q0 + c));
+    unpack8(v, x, c);
+  }
+}
+
+// Write the first n values (n a multiple of 8) of a block, already packed as
+// bf16 pairs, at byte offset `off` of a swizzled stage.
+__device__ __forceinline__ void write_staged_block(uint8_t* stage, uint32_t off, int n, const uint32_t (&pk)[kBlock / 2]) {
+  const uint32_t q0 = off >> 4;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    if (8 * c < n) {
+      const u32x4 v = {pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]};
+      *reinterpret_cast<u32x4*>(stage + 16u * swz(q0 + c)) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // weight kernels (grouped: up to kMaxGroup matrices per launch)
+//
+// A wave works on batches of 64 consecutive blocks of one matrix, one block
+// per lane.  Blocks are numbered row-major, so a batch covers one contiguous
+// byte range of W (rows are contiguous; a tail block holds only its real
+// columns).  The workgroups loop over batches (persistent grid).
 // ---------------------------------------------------------------------------
 
 struct WeightGroup {
-  int32_t n;                        // matrices in this launch
-  int32_t wg_start[kMaxGroup + 1];  // first workgroup of every matrix (prefix sum)
-  uint32_t nblocks[kMaxGroup];      // rows * nb
-  uint32_t nb[kMaxGroup];           // blocks per row
-  int64_t in[kMaxGroup];            // columns
+  int32_t n;                           // matrices in this launch
+  uint32_t total_batches;              // sum of batches over the matrices
+  uint32_t batch_start[kMaxGroup + 1]; // first batch of every matrix (prefix sum)
+  uint32_t nblocks[kMaxGroup];         // rows * nb
+  uint32_t nb[kMaxGroup];              // blocks per row
+  int32_t staged[kMaxGroup];           // 1: W rows start 16-byte aligned (in % 8 == 0, W aligned)
+  int64_t in[kMaxGroup];               // columns
   uint16_t* w[kMaxGroup];
   uint8_t* packed[kMaxGroup];
   uint16_t* norms[kMaxGroup];
 };
 
-// matrix owning this workgroup (uniform across the workgroup)
-__device__ __forceinline__ int group_of(const WeightGroup& g) {
+// matrix owning batch b (uniform across the wave)
+__device__ __forceinline__ int group_of(const WeightGroup& g, uint32_t b) {
   int d = 0;
-  for (int i = 1; i < g.n; ++i) d = (static_cast<int>(blockIdx.x) >= g.wg_start[i]) ? i : d;
+  for (int i = 1; i < g.n; ++i) d = (b >= g.batch_start[i]) ? i : d;
   return d;
 }
 
+struct BatchPos {
+  uint32_t g0, nvalid, lb;
+  int64_t e;  // element offset of this lane's block in W
+  int n;      // real values in this lane's block
+};
+
+__device__ __forceinline__ BatchPos batch_pos(const WeightGroup& g, int d, uint32_t b, int lane) {
+  BatchPos p;
+  p.g0 = (b - g.batch_start[d]) * 64u;
+  const uint32_t left = g.nblocks[d] - p.g0;
+  p.nvalid = left < 64u ? left : 64u;
+  p.lb = p.g0 + (static_cast<uint32_t>(lane) < p.nvalid ? static_cast<uint32_t>(lane) : p.nvalid - 1);
+  const uint32_t nb = g.nb[d];
+  const uint32_t row = p.lb / nb;
+  const uint32_t blk = p.lb - row * nb;
+  const int64_t in = g.in[d];
+  const int64_t col = static_cast<int64_t>(blk) * kBlock;
+  p.e = static_cast<int64_t>(row) * in + col;
+  p.n = static_cast<int>((in - col) < kBlock ? (in - col) : kBlock);
+  return p;
+}
+
 template <int BITS>
-__global__ void __launch_bounds__(kThreads) hlwq_quantize_kernel(const WeightGroup g) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_quantize_kernel(const WeightGroup g) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage_all[kWaves * kStage];
   __shared__ uint2 tab[HLWQ_SEARCH_ENTRIES];
   const uint32_t* src_tab = (BITS == 5) ? c_search5 : c_search3;
   for (int i = threadIdx.x; i < HLWQ_SEARCH_ENTRIES; i += kThreads)
     tab[i] = make_uint2(src_tab[2 * i], src_tab[2 * i + 1]);
   __syncthreads();
 
-  const int d = group_of(g);
-  const uint32_t lb = (blockIdx.x - g.wg_start[d]) * kThreads + threadIdx.x;
-  if (lb >= g.nblocks[d]) return;
-  const uint32_t nb = g.nb[d];
-  const uint32_t row = lb / nb;
-  const uint32_t blk = lb - row * nb;
-  const int64_t in = g.in[d];
-  const int64_t col = static_cast<int64_t>(blk) * kBlock;
-  const int n = static_cast<int>((in - col) < kBlock ? (in - col) : kBlock);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* stage = stage_all + wave * kStage;
+  constexpr uint32_t kOut = 16 * BITS;  // packed bytes per block
 
-  float x[kBlock];
-  load_block(g.w[d] + static_cast<int64_t>(row) * in + col, n, x);
-  const NormInfo ni = norm_info(sumsq_tree(x));
-  fwht(x);
-  uint32_t words[4 * BITS];
-  encode<BITS, kBlock>(x, ni.r, tab, HLWQ_SEARCH_OFFSET, words);
+  for (uint32_t b = blockIdx.x * kWaves + wave; b < g.total_batches; b += gridDim.x * kWaves) {
+    const int d = group_of(g, b);
+    const BatchPos p = batch_pos(g, d, b, lane);
 
-  u32x4* dst = reinterpret_cast<u32x4*>(g.packed[d] + static_cast<size_t>(lb) * (16 * BITS));
+    float x[kBlock];
+    if (g.staged[d]) {
+      const int64_t e0 = first_lane64(p.e);
+      const uint32_t off = static_cast<uint32_t>(p.e - e0) * 2u;
+      const uint32_t end = __builtin_amdgcn_readlane(off + 2u * p.n, p.nvalid - 1);
+      stage_in<16, true>(reinterpret_cast<const uint8_t*>(g.w[d] + e0), end, stage, lane);
+      wait_vmem();
+      read_staged_block(stage, off, p.n, x);
+    } else {
+      load_block(g.w[d] + p.e, p.n, x);
+    }
+
+    const NormInfo ni = norm_info(sumsq_tree(x));
+    fwht(x);
+    uint32_t words[4 * BITS];
+    encode<BITS, kBlock>(x, ni.r, tab, HLWQ_SEARCH_OFFSET, words);
+
+    // packed output of the batch is contiguous: kOut bytes per block
 #pragma unroll
-  for (int q = 0; q < BITS; ++q) {
-    const u32x4 v = {words[4 * q], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]};
-    __builtin_nontemporal_store(v, dst + q);
+    for (int q = 0; q < BITS; ++q) {
+      const u32x4 v = {words[4 * q], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]};
+      *reinterpret_cast<u32x4*>(stage + kOut * lane + 16 * q) = v;
+    }
+    stage_out<BITS, false>(g.packed[d] + static_cast<size_t>(p.g0) * kOut, p.nvalid * kOut, stage, lane);
+    if (static_cast<uint32_t>(lane) < p.nvalid) g.norms[d][p.lb] = ni.n16;
   }
-  g.norms[d][lb] = ni.n16;
 }
 
 template <int BITS>
-__global__ void __launch_bounds__(kThreads) hlwq_dequantize_kernel(const WeightGroup g) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_dequantize_kernel(const WeightGroup g) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage_all[kWaves * kStage];
   __shared__ float cent[1 << BITS];
   const float* src_cent = (BITS == 5) ? c_cent5 : c_cent3;
   if (threadIdx.x < (1 << BITS)) cent[threadIdx.x] = src_cent[threadIdx.x];
   __syncthreads();
 
-  const int d = group_of(g);
-  const uint32_t lb = (blockIdx.x - g.wg_start[d]) * kThreads + threadIdx.x;
-  if (lb >= g.nblocks[d]) return;
-  const uint32_t nb = g.nb[d];
-  const uint32_t row = lb / nb;
-  const uint32_t blk = lb - row * nb;
-  const int64_t in = g.in[d];
-  const int64_t col = static_cast<int64_t>(blk) * kBlock;
-  const int n = static_cast<int>((in - col) < kBlock ? (in - col) : kBlock);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* stage = stage_all + wave * kStage;
+  constexpr uint32_t kIn = 16 * BITS;  // packed bytes per block
 
-  const u32x4* src = reinterpret_cast<const u32x4*>(g.packed[d] + static_cast<size_t>(lb) * (16 * BITS));
-  uint32_t words[4 * BITS];
+  for (uint32_t b = blockIdx.x * kWaves + wave; b < g.total_batches; b += gridDim.x * kWaves) {
+    const int d = group_of(g, b);
+    const BatchPos p = batch_pos(g, d, b, lane);
+
+    stage_in<BITS, false>(g.packed[d] + static_cast<size_t>(p.g0) * kIn, p.nvalid * kIn, stage, lane);
+    const float scale = f16_value(g.norms[d][p.lb]) * 0x1p-7f;
+    wait_vmem();
+    // lanes past the end of the batch read (and later write) the last block
+    const uint32_t slot = p.lb - p.g0;
+    uint32_t words[4 * BITS];
 #pragma unroll
-  for (int q = 0; q < BITS; ++q) {
-    const u32x4 v = __builtin_nontemporal_load(src + q);
-    words[4 * q] = v.x;
-    words[4 * q + 1] = v.y;
-    words[4 * q + 2] = v.z;
-    words[4 * q + 3] = v.w;
+    for (int q = 0; q < BITS; ++q) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + kIn * slot + 16 * q);
+      words[4 * q] = v.x;
+      words[4 * q + 1] = v.y;
+      words[4 * q + 2] = v.z;
+      words[4 * q + 3] = v.w;
+    }
+
+    float v[kBlock];
+    decode<BITS, kBlock>(words, cent, v);
+    fwht(v);
+    uint32_t pk[kBlock / 2];
+#pragma unroll
+    for (int j = 0; j < kBlock; j += 2) pk[j / 2] = pack_bf16x2(v[j] * scale, v[j + 1] * scale);
+
+    if (g.staged[d]) {
+      const int64_t e0 = first_lane64(p.e);
+      const uint32_t off = static_cast<uint32_t>(p.e - e0) * 2u;
+      const uint32_t end = __builtin_amdgcn_readlane(off + 2u * p.n, p.nvalid - 1);
+      // lanes past the end of the batch repeat the last block: identical bytes
+      write_staged_block(stage, off, p.n, pk);
+      stage_out<16, true>(reinterpret_cast<uint8_t*>(g.w[d] + e0), end, stage, lane);
+    } else if (static_cast<uint32_t>(lane) < p.nvalid) {
+      store_block(g.w[d] + p.e, p.n, pk);
+    }
   }
-  const float scale = f16_value(g.norms[d][lb]) * 0x1p-7f;
-
-  float v[kBlock];
-  decode<BITS, kBlock>(words, cent, v);
-  fwht(v);
-#pragma unroll
-  for (int j = 0; j < kBlock; ++j) v[j] = v[j] * scale;
-  store_block(g.w[d] + static_cast<int64_t>(row) * in + col, n, v);
 }
 
 // ---------------------------------------------------------------------------
-// KV-cache kernels: a 256-wide head vector over two adjacent lanes
+// KV-cache kernels: a 256-wide head vector over two adjacent lanes; a wave
+// works on batches of 32 consecutive tokens of one head (16 KB of bf16).
 // ---------------------------------------------------------------------------
 
 struct KvArgs {
@@ -319,77 +472,112 @@ struct KvArgs {
   uint16_t* norms;    // [bh][tq]
   int64_t tokens;
   uint32_t tq;        // quantised tokens per head
-  uint32_t nvec;      // bh * tq
+  uint32_t nbt;       // batches per head, ceil(tq / 32)
+  uint32_t total_batches;
 };
 
-__global__ void __launch_bounds__(kThreads) hlwq_kv_quantize_kernel(const KvArgs a) {
+struct KvPos {
+  uint32_t bh, t0, nvalid, t, half;
+};
+
+__device__ __forceinline__ KvPos kv_pos(const KvArgs& a, uint32_t b, int lane) {
+  KvPos p;
+  p.bh = b / a.nbt;
+  p.t0 = (b - p.bh * a.nbt) * 32u;
+  const uint32_t left = a.tq - p.t0;
+  p.nvalid = left < 32u ? left : 32u;
+  const uint32_t v = static_cast<uint32_t>(lane) >> 1;
+  p.t = p.t0 + (v < p.nvalid ? v : p.nvalid - 1);
+  p.half = lane & 1;  // 0: entries 0..127, 1: entries 128..255
+  return p;
+}
+
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_kv_quantize_kernel(const KvArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage_all[kWaves * kStage];
   __shared__ uint2 tab[HLWQ_KV_SEARCH_ENTRIES];
   for (int i = threadIdx.x; i < HLWQ_KV_SEARCH_ENTRIES; i += kThreads)
     tab[i] = make_uint2(c_kvsearch3[2 * i], c_kvsearch3[2 * i + 1]);
   __syncthreads();
 
-  const uint32_t gid = blockIdx.x * kThreads + threadIdx.x;
-  const uint32_t vec = gid >> 1;
-  const uint32_t half = gid & 1u;  // 0: entries 0..127, 1: entries 128..255
-  if (vec >= a.nvec) return;       // both lanes of a vector leave together
-  const uint32_t bh = vec / a.tq;
-  const uint32_t t = vec - bh * a.tq;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* stage = stage_all + wave * kStage;
 
-  float x[kBlock];
-  load_block(a.kv + (static_cast<int64_t>(bh) * a.tokens + t) * kKvDim + half * kBlock, kBlock, x);
-  // last tree level joins the two halves: lower half first (addition commutes)
-  const float s_half = sumsq_tree(x);
-  const NormInfo ni = norm_info(s_half + lane_xor1(s_half));
-  fwht(x);
-  // stride-128 stage across the lane pair: (a, b) -> (a + b, a - b)
-  const float sgn = half ? -1.0f : 1.0f;
-#pragma unroll
-  for (int j = 0; j < kBlock; ++j) x[j] = __builtin_fmaf(x[j], sgn, lane_xor1(x[j]));
+  for (uint32_t b = blockIdx.x * kWaves + wave; b < a.total_batches; b += gridDim.x * kWaves) {
+    const KvPos p = kv_pos(a, b, lane);
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv + (static_cast<int64_t>(p.bh) * a.tokens + p.t0) * kKvDim);
+    stage_in<16, true>(src, p.nvalid * 2u * kKvDim, stage, lane);
+    wait_vmem();
+    float x[kBlock];
+    read_staged_block(stage, (p.t - p.t0) * 2u * kKvDim + p.half * 2u * kBlock, kBlock, x);
 
-  uint32_t words[12];
-  encode<3, kBlock>(x, ni.r, tab, HLWQ_KV_SEARCH_OFFSET, words);
-  u32x4* dst = reinterpret_cast<u32x4*>(a.packed + static_cast<size_t>(vec) * 96 + half * 48);
+    // last tree level joins the two halves (addition commutes, so both lanes agree)
+    const float s_half = sumsq_tree(x);
+    const NormInfo ni = norm_info(s_half + lane_xor1(s_half));
+    fwht(x);
+    // stride-128 stage across the lane pair: (a, b) -> (a + b, a - b)
+    const float sgn = pair_sign(p.half);
 #pragma unroll
-  for (int q = 0; q < 3; ++q) {
-    const u32x4 v = {words[4 * q], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]};
-    __builtin_nontemporal_store(v, dst + q);
+    for (int j = 0; j < kBlock; ++j) x[j] = cross_pair(x[j], sgn);
+
+    uint32_t words[12];
+    encode<3, kBlock>(x, ni.r, tab, HLWQ_KV_SEARCH_OFFSET, words);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const u32x4 v = {words[4 * q], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]};
+      *reinterpret_cast<u32x4*>(stage + 48 * lane + 16 * q) = v;
+    }
+    const size_t vec0 = static_cast<size_t>(p.bh) * a.tq + p.t0;
+    stage_out<3, false>(a.packed + vec0 * 96, p.nvalid * 96u, stage, lane);
+    if (p.half == 0 && (static_cast<uint32_t>(lane) >> 1) < p.nvalid) a.norms[vec0 + (lane >> 1)] = ni.n16;
   }
-  if (half == 0) a.norms[vec] = ni.n16;
 }
 
-__global__ void __launch_bounds__(kThreads) hlwq_kv_dequantize_kernel(const KvArgs a) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_kv_dequantize_kernel(const KvArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage_all[kWaves * kStage];
   __shared__ float cent[8];
   if (threadIdx.x < 8) cent[threadIdx.x] = c_cent3[threadIdx.x];
   __syncthreads();
 
-  const uint32_t gid = blockIdx.x * kThreads + threadIdx.x;
-  const uint32_t vec = gid >> 1;
-  const uint32_t half = gid & 1u;
-  if (vec >= a.nvec) return;
-  const uint32_t bh = vec / a.tq;
-  const uint32_t t = vec - bh * a.tq;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* stage = stage_all + wave * kStage;
 
-  const u32x4* src = reinterpret_cast<const u32x4*>(a.packed + static_cast<size_t>(vec) * 96 + half * 48);
-  uint32_t words[12];
+  for (uint32_t b = blockIdx.x * kWaves + wave; b < a.total_batches; b += gridDim.x * kWaves) {
+    const KvPos p = kv_pos(a, b, lane);
+    const size_t vec0 = static_cast<size_t>(p.bh) * a.tq + p.t0;
+    stage_in<3, false>(a.packed + vec0 * 96, p.nvalid * 96u, stage, lane);
+    const float scale = f16_value(a.norms[vec0 + (p.t - p.t0)]) * 0x1p-8f;
+    wait_vmem();
+    // lanes past the end of the batch read (and later write) the last vector
+    const uint32_t slot = 2u * (p.t - p.t0) + p.half;
+    uint32_t words[12];
 #pragma unroll
-  for (int q = 0; q < 3; ++q) {
-    const u32x4 v = __builtin_nontemporal_load(src + q);
-    words[4 * q] = v.x;
-    words[4 * q + 1] = v.y;
-    words[4 * q + 2] = v.z;
-    words[4 * q + 3] = v.w;
+    for (int q = 0; q < 3; ++q) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + 48 * slot + 16 * q);
+      words[4 * q] = v.x;
+      words[4 * q + 1] = v.y;
+      words[4 * q + 2] = v.z;
+      words[4 * q + 3] = v.w;
+    }
+
+    float v[kBlock];
+    decode<3, kBlock>(words, cent, v);
+    fwht(v);
+    // stride-128 stage across the lane pair, then scale and round to bf16
+    const float sgn = pair_sign(p.half);
+    uint32_t pk[kBlock / 2];
+#pragma unroll
+    for (int j = 0; j < kBlock; j += 2)
+      pk[j / 2] = pack_bf16x2(cross_pair(v[j], sgn) * scale, cross_pair(v[j + 1], sgn) * scale);
+
+    // lanes past the end of the batch repeat the last vector: identical bytes
+    // to the same place, so the write needs no lane mask (a masked region
+    // would keep the DPP operands from folding)
+    write_staged_block(stage, (p.t - p.t0) * 2u * kKvDim + p.half * 2u * kBlock, kBlock, pk);
+    uint8_t* dst = reinterpret_cast<uint8_t*>(a.kv + (static_cast<int64_t>(p.bh) * a.tokens + p.t0) * kKvDim);
+    stage_out<16, true>(dst, p.nvalid * 2u * kKvDim, stage, lane);
   }
-  const float scale = f16_value(a.norms[vec]) * 0x1p-8f;
-
-  float v[kBlock];
-  decode<3, kBlock>(words, cent, v);
-  fwht(v);
-  const float sgn = half ? -1.0f : 1.0f;
-#pragma unroll
-  for (int j = 0; j < kBlock; ++j) v[j] = __builtin_fmaf(v[j], sgn, lane_xor1(v[j]));
-#pragma unroll
-  for (int j = 0; j < kBlock; ++j) v[j] = v[j] * scale;
-  store_block(a.kv + (static_cast<int64_t>(bh) * a.tokens + t) * kKvDim + half * kBlock, kBlock, v);
 }
 
 // ---------------------------------------------------------------------------
@@ -424,6 +612,23 @@ int check_weight_desc(const hlwq_mat_desc& m, int64_t* blocks) {
   return HLWQ_OK;
 }
 
+// Resident workgroups per launch: enough to fill every CU twice (the
+// kernels use ~200 VGPRs and 64 KB of LDS per workgroup, so two fit on a CU);
+// the workgroups loop over batches.
+uint32_t persistent_grid(uint32_t batches) {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  int n = dev < 64 ? cus[dev].load(std::memory_order_relaxed) : 0;
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    if (dev < 64) cus[dev].store(n, std::memory_order_relaxed);
+  }
+  const uint64_t want = (static_cast<uint64_t>(batches) + kWaves - 1) / kWaves;
+  const uint64_t cap = static_cast<uint64_t>(n) * 2;
+  return static_cast<uint32_t>(want < cap ? want : cap);
+}
+
 template <bool QUANT>
 int run_weight_group(const hlwq_mat_desc* mats, int n, int bits, hipStream_t stream) {
   if (n < 0) return HLWQ_ERR_SHAPE;
@@ -439,25 +644,27 @@ int run_weight_group(const hlwq_mat_desc* mats, int n, int bits, hipStream_t str
   while (i < n) {
     WeightGroup g;
     std::memset(&g, 0, sizeof(g));
-    int64_t wg = 0;
+    int64_t batches = 0;
     for (; i < n && g.n < kMaxGroup; ++i) {
       int64_t nblk;
       check_weight_desc(mats[i], &nblk);
       if (nblk == 0) continue;
       const int k = g.n++;
-      g.wg_start[k] = static_cast<int32_t>(wg);
+      g.batch_start[k] = static_cast<uint32_t>(batches);
       g.nblocks[k] = static_cast<uint32_t>(nblk);
       g.nb[k] = static_cast<uint32_t>(ceil_div(mats[i].in, kBlock));
       g.in[k] = mats[i].in;
       g.w[k] = static_cast<uint16_t*>(mats[i].w);
       g.packed[k] = static_cast<uint8_t*>(mats[i].packed);
       g.norms[k] = static_cast<uint16_t*>(mats[i].norms);
-      wg += ceil_div(nblk, kThreads);
-      if (wg > 0x7fffffff) return HLWQ_ERR_LIMIT;
+      g.staged[k] = (mats[i].in % 8 == 0) && ((reinterpret_cast<uintptr_t>(mats[i].w) & 15u) == 0);
+      batches += ceil_div(nblk, 64);
+      if (batches > 0x7fffffff) return HLWQ_ERR_LIMIT;
     }
     if (g.n == 0) continue;
-    g.wg_start[g.n] = static_cast<int32_t>(wg);
-    const dim3 grid(static_cast<uint32_t>(wg)), block(kThreads);
+    g.batch_start[g.n] = static_cast<uint32_t>(batches);
+    g.total_batches = static_cast<uint32_t>(batches);
+    const dim3 grid(persistent_grid(g.total_batches)), block(kThreads);
     if (QUANT) {
       if (bits == 5) hipLaunchKernelGGL(hlwq_quantize_kernel<5>, grid, block, 0, stream, g);
       else hipLaunchKernelGGL(hlwq_quantize_kernel<3>, grid, block, 0, stream, g);
@@ -500,7 +707,7 @@ int run_kv(bool quant, const void* kv, void* packed, void* norms, int64_t batch,
   if (!kv || !packed || !norms) return HLWQ_ERR_NULL;
   if (nvec > 0x3fffffff || tq > 0x7fffffff) return HLWQ_ERR_LIMIT;
   if ((reinterpret_cast<uintptr_t>(packed) & 15u) || (reinterpret_cast<uintptr_t>(norms) & 1u) ||
-      (reinterpret_cast<uintptr_t>(kv) & 1u))
+      (reinterpret_cast<uintptr_t>(kv) & 15u))
     return HLWQ_ERR_ALIGN;
   KvArgs a;
   a.kv = const_cast<uint16_t*>(static_cast<const uint16_t*>(kv));
@@ -508,8 +715,11 @@ int run_kv(bool quant, const void* kv, void* packed, void* norms, int64_t batch,
   a.norms = static_cast<uint16_t*>(norms);
   a.tokens = tokens;
   a.tq = static_cast<uint32_t>(tq);
-  a.nvec = static_cast<uint32_t>(nvec);
-  const dim3 grid(static_cast<uint32_t>(ceil_div(2 * nvec, kThreads))), block(kThreads);
+  a.nbt = static_cast<uint32_t>(ceil_div(tq, 32));
+  int64_t batches;
+  if (!mul_ok(bh, a.nbt, &batches) || batches > 0x7fffffff) return HLWQ_ERR_LIMIT;
+  a.total_batches = static_cast<uint32_t>(batches);
+  const dim3 grid(persistent_grid(a.total_batches)), block(kThreads);
   if (quant) hipLaunchKernelGGL(hlwq_kv_quantize_kernel, grid, block, 0, stream, a);
   else hipLaunchKernelGGL(hlwq_kv_dequantize_kernel, grid, block, 0, stream, a);
   return launch_status();
