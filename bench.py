@@ -78,6 +78,29 @@ def stored_traffic(config):
         return None
 
 
+def copy_ceiling(torch, dev, nbytes, reps=10):
+    """Device-to-device copy moving the same number of bytes (half read, half
+    written) as one quantize or dequantize launch: the practical HBM ceiling."""
+    n = nbytes // 4  # bytes read = bytes written = nbytes / 2
+    src = torch.empty(n // 2, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    moved = 2 * src.numel() * 4
+    del src, dst
+    return {"gbs": round(moved / (ms * 1e-3) / 1e9, 1), "bytes": moved, "ms": round(ms, 4),
+            "kernel": "torch copy_ (float32 device-to-device)"}
+
+
 def cpu_baseline(config, budget_s=12.0):
     """The oracle (fp32 canonical tier) on whole expert matrices until the budget is used."""
     from oracle import hlwq_ref as ref
@@ -205,6 +228,8 @@ def main():
                        "gbs": round(d_gbs, 1), "weights_per_s": weights / (d_ms.mean() * 1e-3)},
         "roofline": roofline,
     }
+    result["copy_ceiling"] = copy_ceiling(torch, dev, bytes_dir)
+    result["copy_frac"] = round(2 * bytes_dir / (ms_per_step * 1e-3) / 1e9 / result["copy_ceiling"]["gbs"], 4)
     del qitems, ditems
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
