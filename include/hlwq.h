@@ -16,8 +16,9 @@
  *
  * Arithmetic.  Every kernel follows one fixed IEEE-fp32 operation order, so
  * results are bit-identical run to run and device to device:
- *   norm   : squares summed by an adjacent-pair tree, correctly rounded sqrt,
- *            fp16 by round-to-nearest-even;
+ *   norm   : squares summed by an adjacent-pair tree whose first level forms
+ *            each pair as one fused multiply-add, RN(x0^2 + RN(x1^2)); then a
+ *            correctly rounded sqrt, fp16 by round-to-nearest-even;
  *   rotate : unnormalised +-1 butterflies (a, b) -> (a + b, a - b) at strides
  *            1, 2, 4, ... (natural / Sylvester order), then y = z * (1 / n),
  *            1 / n correctly rounded, and 0 for blocks whose norm is below the
@@ -144,14 +145,16 @@ size_t hlwq_norm_count(int64_t rows, int64_t in, int block);
  * 2^bits - 1 decision thresholds.  bits = 5 or 3.  Host-only, no GPU needed. */
 int hlwq_centroids(int bits, float* centroids, float* thresholds);
 
-/* Copy the bucket table the kernels use to find a code with one compare:
- * entries of {threshold bits (fp32, +inf if the bucket holds none), count of
- * thresholds below the bucket}; a value y falls in entry
- * (uint32_t) fmaf(y, 8, offset).  kind 0: Q5 weights (offset 96), 1: Q3
- * weights (offset 96), 2: Q3 KV (offset 136).  Writes at most `capacity`
- * pairs into `words` (2 * capacity uint32) and returns the entry count, or a
- * negative status.  Host-only; exposed so the table can be verified. */
-int hlwq_search_table(int kind, uint32_t* words, int capacity, float* offset);
+/* Copy the bucket table the kernels use to find a code with one compare.
+ * For a rotated value y the kernels form u = y + offset in fp32 and read the
+ * 16-byte entry at byte offset (bits(u) & mask) of the table: {threshold bits
+ * (fp32, +inf if the bucket holds none), count of thresholds below the bucket,
+ * 0, 0}; the code is count + (y > threshold).  kind 0: Q5 weights, 1: Q3
+ * weights, 2: Q3 KV.  Copies at most `capacity` entries (4 * capacity
+ * uint32) into `words` (may be NULL), stores the offset and mask, and returns
+ * the entry count, or a negative status.  Host-only; exposed so the table can
+ * be verified. */
+int hlwq_search_table(int kind, uint32_t* words, int capacity, float* offset, uint32_t* mask);
 
 /* Static, human-readable text for a status code. */
 const char* hlwq_status_string(int status);

@@ -29,9 +29,11 @@ Two tiers:
 * Tier C ("canonical", fp32): one fixed IEEE-fp32 operation sequence for the
   same map.  Every operation is a single correctly rounded numpy float32 op, so
   the rounding of every intermediate is defined.  Readings taken here:
-    - the norm is an adjacent-pair tree over the squares (level l adds the
-      partial sums 2i and 2i+1), then a correctly rounded sqrt; fp16 by
-      round-to-nearest-even from that fp32 value;
+    - the norm is an adjacent-pair tree over the squares: level 0 forms each
+      pair x_2i^2 + x_2i+1^2 with one rounding of x_2i^2 + RN(x_2i+1^2) (a
+      fused multiply-add), level l adds the partial sums 2i and 2i+1; then a
+      correctly rounded sqrt; fp16 by round-to-nearest-even from that fp32
+      value;
     - normalise-then-rotate is carried out as rotate-then-scale (the map is
       linear, one rounding fewer): the unnormalised +-1 butterflies
       (a, b) -> (a + b, a - b) at strides 1, 2, 4, ..., then y = z * (1/n) with
@@ -193,9 +195,29 @@ def dequantize_def(codes: np.ndarray, norms: np.ndarray, bits: int,
 # Tier C: canonical fp32 operation order
 # --------------------------------------------------------------------------
 
+def pair_sumsq_f32(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """RN32(a*a + RN32(b*b)): one pair of squares as a fused multiply-add forms it.
+
+    a*a is exact in fp64 for bf16 a (at most 16 significant bits) and RN32(b*b)
+    is an fp32 value, so their fp64 sum is either exact or lies so close to one
+    of the two terms (the other below 2^-29 of it, far from any fp32 rounding
+    boundary) that rounding it to fp32 gives the correctly rounded sum.
+    """
+    a = np.asarray(a, dtype=np.float32)
+    b = np.asarray(b, dtype=np.float32)
+    a2 = a.astype(np.float64) * a.astype(np.float64)
+    b2 = (b * b).astype(np.float64)
+    return (a2 + b2).astype(np.float32)
+
+
 def norm_tree_f32(x: np.ndarray) -> np.ndarray:
-    """Sum of squares by the adjacent-pair tree, then a correctly rounded sqrt."""
-    s = np.asarray(x, dtype=np.float32) * np.asarray(x, dtype=np.float32)
+    """Sum of squares by the adjacent-pair tree, then a correctly rounded sqrt.
+
+    Level 0 forms every pair (x_2i, x_2i+1) as RN(x_2i^2 + RN(x_2i+1^2)) (one
+    fused multiply-add); every further level adds neighbouring partial sums.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    s = pair_sumsq_f32(x[..., 0::2], x[..., 1::2])
     while s.shape[-1] > 1:
         s = s[..., 0::2] + s[..., 1::2]
     return np.sqrt(s[..., 0])

@@ -37,13 +37,14 @@ def test_codebook_matches_oracle(bits):
     assert np.array_equal(t.view(np.uint32), ot.view(np.uint32))
 
 
-def _bucket_codes(table, offset, y):
-    # k = (uint32) fmaf(y, 8, offset): 8y + offset is exact in fp64 for fp32 y,
-    # so one rounding to fp32 reproduces the fused multiply-add.
-    u = (np.asarray(y, np.float32).astype(np.float64) * 8.0 + offset).astype(np.float32)
-    k = np.where(u > 0, np.trunc(u), 0).astype(np.int64)
+def _bucket_codes(table, offset, mask, y):
+    # u = y + offset with one fp32 rounding: the fp64 sum is exact whenever the
+    # fp32 rounding of it matters, so rounding it to fp32 reproduces the add.
+    y = np.asarray(y, np.float32)
+    u = (y.astype(np.float64) + np.float64(offset)).astype(np.float32)
+    k = (u.view(np.uint32) & np.uint32(mask)) >> 4
     thr = table[k, 0].view(np.float32)
-    return table[k, 1].astype(np.int64) + (np.asarray(y, np.float32) > thr)
+    return table[k, 1].astype(np.int64) + (y > thr)
 
 
 @pytest.mark.parametrize("kind,bits,limit", [(0, 5, 11.32), (1, 3, 11.32), (2, 3, 16.0)])
@@ -51,20 +52,24 @@ def test_bucket_table_reproduces_threshold_count(kind, bits, limit):
     # The kernels find codes with one table read and one compare; on every
     # fp32 value near a threshold or a bucket edge, and on a dense sweep of the
     # reachable range, that must equal the oracle's threshold count.
-    table, offset = wq.hlwq_search_table(kind)
+    table, offset, mask = wq.hlwq_search_table(kind)
     _, b32 = lm.table(bits)
-    assert table.shape[0] * 1.0 > 8 * limit + offset
-    probes = np.concatenate([b32, (np.arange(table.shape[0] + 1) - offset) / 8.0]).astype(np.float32)
-    steps = np.arange(-2048, 2049, dtype=np.int64)
-    near = (probes.view(np.int32).astype(np.int64)[:, None] + steps[None, :])
-    pos = near[probes[:, None].repeat(steps.size, 1) >= 0]
-    y_near = np.concatenate([pos.astype(np.int32).view(np.float32),
-                             (-(pos.astype(np.int32).view(np.float32)))])
+    assert table.shape[0] == (mask >> 4) + 1
+    half = table.shape[0] / 16.0
+    assert limit < half - 0.25
+    edges = (98304.0 + np.arange(table.shape[0] + 1) / 8.0 - offset)
+    probes = np.concatenate([b32, edges]).astype(np.float32)
+    steps = np.arange(-4096, 4097, dtype=np.int64)
+    near = []
+    for p in probes:
+        bits_p = np.abs(p).view(np.int32).astype(np.int64) + steps
+        v = bits_p[bits_p >= 0].astype(np.int32).view(np.float32)
+        near.append(np.copysign(v, p) if p != 0 else np.concatenate([v, -v]))
     rng = np.random.default_rng(0)
-    y = np.concatenate([y_near, np.linspace(-limit, limit, 2_000_001, dtype=np.float32),
-                        rng.standard_normal(200_000).astype(np.float32), np.float32([0.0, -0.0])])
+    y = np.concatenate(near + [np.linspace(-limit, limit, 2_000_001, dtype=np.float32),
+                               rng.standard_normal(200_000).astype(np.float32), np.float32([0.0, -0.0])])
     y = y[np.abs(y) <= limit]
-    assert np.array_equal(_bucket_codes(table, offset, y), ref.codes_from_y(y, b32))
+    assert np.array_equal(_bucket_codes(table, offset, mask, y), ref.codes_from_y(y, b32))
 
 
 def test_size_helpers():

@@ -1,6 +1,7 @@
 """Pins for the oracle's rotation, norm and packing steps (CPU only)."""
 import json
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -153,3 +154,36 @@ def test_storage_density():
     assert 80 / 128 == 0.625
     total = 33.62e9 * (80 + 2) / 128
     assert abs(total / 21.55e9 - 1) < 1e-3
+
+
+def _rn32(q: Fraction) -> np.float32:
+    """Round an exact rational to the nearest fp32 (ties to even) by search."""
+    f = np.float32(float(q))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    return min(cands, key=lambda v: (abs(Fraction(float(v)) - q), int(np.float32(v).view(np.uint32)) & 1))
+
+
+def test_first_tree_level_is_a_fused_pair():
+    # RN(a^2 + RN(b^2)) with exact rationals, on normal, tiny (squares in the
+    # fp32 denormal range) and mixed-magnitude bf16 pairs; a two-rounding
+    # RN(RN(a^2) + RN(b^2)) differs from it on some of the tiny ones.
+    rng = np.random.default_rng(6)
+    mags = np.exp(rng.uniform(-105, 40, (4000, 2)))
+    v = synth_bf16((rng.standard_normal((4000, 2)) * mags).astype(np.float32))
+    a, b = v[:, 0], v[:, 1]
+    got = ref.pair_sumsq_f32(a, b)
+    want = np.array([_rn32(Fraction(float(x)) ** 2 + Fraction(float(np.float32(y) * np.float32(y))))
+                     for x, y in zip(a, b)], dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # a pair whose squares fall in the fp32 denormal range, where rounding the
+    # first square separately changes the sum: 2^-138 * 1.125^2 + 2^-140 * 1.546875^2
+    a = np.uint32([0x1B900000]).view(np.float32)
+    b = np.uint32([0x1B460000]).view(np.float32)
+    fused = ref.pair_sumsq_f32(a, b)[0]
+    assert fused == _rn32(Fraction(float(a[0])) ** 2 + Fraction(float(b[0] * b[0])))
+    assert fused != np.float32(a[0] * a[0] + b[0] * b[0])
+
+
+def synth_bf16(x):
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return (((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint32) << 16).view(np.float32)

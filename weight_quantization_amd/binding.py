@@ -54,7 +54,8 @@ _SIGNATURES = {
     "hlwq_kv_dequantize": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _i64, _vp, _vp]),
     "hlwq_packed_bytes": (ctypes.c_size_t, [_i64, _i64, _int, _int]),
     "hlwq_norm_count": (ctypes.c_size_t, [_i64, _i64, _int]),
-    "hlwq_search_table": (_int, [_int, ctypes.POINTER(ctypes.c_uint32), _int, ctypes.POINTER(ctypes.c_float)]),
+    "hlwq_search_table": (_int, [_int, ctypes.POINTER(ctypes.c_uint32), _int, ctypes.POINTER(ctypes.c_float),
+                                 ctypes.POINTER(ctypes.c_uint32)]),
     "hlwq_status_string": (ctypes.c_char_p, [_int]),
 }
 _SIGNATURES["hlwq_centroids"] = (_int, [_int, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)])
@@ -116,15 +117,16 @@ def hlwq_centroids(bits: int):
 
 
 def hlwq_search_table(kind: int):
-    """(entries uint32[n, 2] = {threshold bits, base}, offset) of a bucket table."""
+    """(entries uint32[n, 4] = {threshold bits, base, 0, 0}, offset, mask) of a bucket table."""
     lib = load_library()
     off = ctypes.c_float()
-    n = lib.hlwq_search_table(kind, None, 0, ctypes.byref(off))
+    mask = ctypes.c_uint32()
+    n = lib.hlwq_search_table(kind, None, 0, ctypes.byref(off), ctypes.byref(mask))
     if n < 0:
         _check("hlwq_search_table", n)
-    buf = (ctypes.c_uint32 * (2 * n))()
-    lib.hlwq_search_table(kind, buf, n, ctypes.byref(off))
-    return np.frombuffer(buf, dtype=np.uint32).reshape(n, 2).copy(), float(off.value)
+    buf = (ctypes.c_uint32 * (4 * n))()
+    lib.hlwq_search_table(kind, buf, n, ctypes.byref(off), ctypes.byref(mask))
+    return np.frombuffer(buf, dtype=np.uint32).reshape(n, 4).copy(), float(off.value), int(mask.value)
 
 
 # --------------------------------------------------------------------------

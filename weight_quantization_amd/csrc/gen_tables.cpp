@@ -10,26 +10,28 @@
 //     strictly below y" is the index of the nearest centroid, ties low;
 //   * the bucket table the kernels use to find a code with one compare.
 //
-// Bucket search.  For a rotated value y the kernels form
-//   k = (uint32_t) fmaf(y, 8, 96)            (round to nearest, then truncate)
-// and read entry k = {threshold t_k or +inf, base_k}; the code is
-//   base_k + (y > t_k).
-// Bucket k nominally holds y in [(k - 96) / 8, (k - 95) / 8).  Because the
-// buckets are narrower than the smallest gap between thresholds, each holds at
-// most one threshold; base_k counts the thresholds below the bucket.  Rounding
-// in the fma can only move a y that lies just below a bucket edge up into the
-// next bucket (rounding is monotone and the edges are representable), so the
-// result stays exact as long as no threshold lies within that rounding
-// distance below an edge.  This program checks that condition with a wide
-// margin and then verifies the search by brute force against the plain count
-// on every fp32 value near every threshold and edge, plus a dense sweep; it
-// exits non-zero, failing the build, if anything disagrees.
+// Bucket search.  For a rotated value y the kernels form, in fp32,
+//   u = y + O            (one rounding; O lies in [2^16, 2^17), ulp 1/128)
+// and read the entry at LDS byte offset  bits(u) & MASK.  Every u the kernels
+// can produce lies in one aligned window of that binade in which the masked
+// mantissa bits count buckets of width 1/8 (16 ulps), so the masked bits are
+// the byte offset of a 16-byte entry with no shift.  The entry is
+// {threshold t_k or +inf, base_k} and the code is base_k + (y > t_k).
+// Buckets are narrower than the smallest gap between thresholds, so each holds
+// at most one threshold; base_k counts the thresholds below the bucket.  The
+// add is monotone and the bucket edges are representable, so rounding can only
+// move a y lying at most 1/256 below an edge up into the next bucket; the
+// result stays exact as long as no threshold lies that close below an edge.
+// The phase of the edges (O modulo 1/8) is chosen per table to keep every
+// threshold at least 1/128 below the next edge; this program then verifies the
+// search by brute force against the plain count on every fp32 value near
+// every threshold and edge, plus a dense sweep, and exits non-zero (failing
+// the build) on any disagreement.
 //
-// |y| <= sqrt(128) * (1 + 2e-6) for every finite block (Cauchy-Schwarz on the
-// unit-norm rotated block), so k stays inside [5, 187) and 192 entries cover
-// every reachable bucket; the same bound holds for the 256-wide KV vectors,
-// whose values are at most sqrt(256) = 16 in magnitude, so their table is
-// indexed with fmaf(y, 8, 136) into 272 entries.
+// |y| <= sqrt(128) * (1 + 2e-6) for every finite 128-block (Cauchy-Schwarz on
+// the unit-norm rotated block), inside the 32-wide window of the weight
+// tables (256 entries, MASK 0xff0); 256-wide KV vectors reach |y| <= 16, so
+// their table spans a 64-wide window (512 entries, MASK 0x1ff0).
 
 #include <cinttypes>
 #include <cmath>
@@ -96,7 +98,9 @@ uint32_t f2u(float f) {
 struct Tables {
   int K;
   std::vector<float> cent, thr;
-  std::vector<uint32_t> search;  // pairs {threshold bits, base}
+  std::vector<uint32_t> search;  // 16-byte entries {threshold bits, base, 0, 0}
+  float offset = 0.0f;           // O
+  uint32_t mask = 0;             // byte-offset mask of bits(u)
 };
 
 // code by definition: number of thresholds strictly below y
@@ -106,18 +110,28 @@ uint32_t count_code(const std::vector<float>& thr, float y) {
   return n;
 }
 
-uint32_t bucket_code(const Tables& tb, float y, float offset) {
-  const float u = std::fmaf(y, 8.0f, offset);
-  const uint32_t k = u > 0.0f ? (uint32_t)u : 0u;  // device: v_cvt_u32_f32 saturates at 0
+constexpr double kU0 = 98304.0;  // 1.5 * 2^16: start of the window, low 13 mantissa bits zero
+
+uint32_t bucket_code(const Tables& tb, float y) {
+  const float u = y + tb.offset;  // one fp32 rounding, as on the device
+  uint32_t bits;
+  std::memcpy(&bits, &u, 4);
+  const uint32_t k = (bits & tb.mask) >> 4;
   float t;
-  uint32_t bits = tb.search[2 * k];
-  std::memcpy(&t, &bits, 4);
-  return tb.search[2 * k + 1] + ((y > t) ? 1u : 0u);
+  std::memcpy(&t, &tb.search[4 * k], 4);
+  return tb.search[4 * k + 1] + ((y > t) ? 1u : 0u);
 }
 
-Tables make_tables(int K, int entries, int offset) {
+// y-interval [lo, hi) of bucket k for window offset O
+void bucket_range(int k, double O, double* lo, double* hi) {
+  *lo = kU0 + k / 8.0 - O;
+  *hi = kU0 + (k + 1) / 8.0 - O;
+}
+
+Tables make_tables(int K, int entries, uint32_t mask) {
   Tables tb;
   tb.K = K;
+  tb.mask = mask;
   const std::vector<double> c = lloyd_max(K);
   for (double v : c) tb.cent.push_back((float)v);
   for (int k = 0; k + 1 < K; ++k) {
@@ -126,38 +140,60 @@ Tables make_tables(int K, int entries, int offset) {
     if ((double)b > m) b = std::nextafterf(b, -INFINITY);
     tb.thr.push_back(b);
   }
-  // bucket table
-  const double margin = std::ldexp(1.0, -18);
+  // window centred on y = 0; the phase (steps of 1/64) is chosen to keep the
+  // largest distance between every threshold and the bucket edge above it
+  // (only a value just below an edge can be rounded into the next bucket)
+  const double half = entries / 16.0;  // half the window width in y
+  double best_phase = -1, best_gap = -1;
+  for (int j = 0; j < 16; ++j) {
+    const double phase = j / 128.0;
+    double gap = 1e9;
+    for (float t : tb.thr) {
+      const double r = std::fmod((double)t + half + phase, 0.125);  // position inside its bucket
+      const double rr = r < 0 ? r + 0.125 : r;
+      gap = std::fmin(gap, 0.125 - rr);
+    }
+    if (gap > best_gap) { best_gap = gap; best_phase = phase; }
+  }
+  if (best_gap < 1.0 / 128.0) {
+    std::fprintf(stderr, "gen_tables: no bucket phase keeps thresholds 1/128 below the edges (K=%d)\n", K);
+    std::exit(1);
+  }
+  const double O = kU0 + half + best_phase;
+  tb.offset = (float)O;
+  if ((double)tb.offset != O) {
+    std::fprintf(stderr, "gen_tables: window offset not representable\n");
+    std::exit(1);
+  }
   for (int k = 0; k < entries; ++k) {
-    const double lo = (k - offset) / 8.0, hi = (k - offset + 1) / 8.0;
+    double lo, hi;
+    bucket_range(k, O, &lo, &hi);
     uint32_t base = 0;
     int inside = 0;
     float t_in = INFINITY;
     for (float t : tb.thr) {
       if ((double)t < lo) ++base;
       else if ((double)t < hi) { ++inside; t_in = t; }
-      if ((double)t > lo - margin && (double)t < lo) {
-        std::fprintf(stderr, "gen_tables: threshold %.9g too close below bucket edge %.9g\n", t, lo);
-        std::exit(1);
-      }
     }
     if (inside > 1) {
       std::fprintf(stderr, "gen_tables: bucket %d holds %d thresholds\n", k, inside);
       std::exit(1);
     }
-    if (k == 0 && inside) {
-      std::fprintf(stderr, "gen_tables: lowest bucket must hold no threshold\n");
-      std::exit(1);
-    }
     tb.search.push_back(f2u(t_in));
     tb.search.push_back(base);
+    tb.search.push_back(0u);
+    tb.search.push_back(0u);
   }
-  // brute-force verification of the bucketed search
-  const float foff = (float)offset;
-  const float ymax = (entries - offset) / 8.0f - 0.25f;
+  // brute-force verification over the reachable range |y| < half - 1/8
+  const float ymax = (float)(half - 0.25);
   std::vector<float> probes;
   for (float t : tb.thr) probes.push_back(t);
-  for (int k = 0; k <= entries; ++k) probes.push_back((k - offset) / 8.0f);
+  for (int k = 0; k <= entries; ++k) {
+    double lo, hi;
+    bucket_range(k, O, &lo, &hi);
+    probes.push_back((float)lo);
+  }
+  probes.push_back(0.0f);
   for (float p : probes) {
     float lo = p, hi = p;
     for (int i = 0; i < 4096; ++i) {
@@ -165,7 +201,7 @@ Tables make_tables(int K, int entries, int offset) {
       hi = std::nextafterf(hi, INFINITY);
       for (float y : {lo, hi, p}) {
         if (!(std::fabs(y) < ymax)) continue;
-        if (count_code(tb.thr, y) != bucket_code(tb, y, foff)) {
+        if (count_code(tb.thr, y) != bucket_code(tb, y)) {
           std::fprintf(stderr, "gen_tables: bucket search wrong at y=%a\n", y);
           std::exit(1);
         }
@@ -174,13 +210,13 @@ Tables make_tables(int K, int entries, int offset) {
   }
   for (int64_t i = -20000000; i <= 20000000; ++i) {
     const float y = (float)((double)i * (ymax / 20000000.0));
-    if (count_code(tb.thr, y) != bucket_code(tb, y, foff)) {
+    if (count_code(tb.thr, y) != bucket_code(tb, y)) {
       std::fprintf(stderr, "gen_tables: bucket search wrong at y=%a\n", y);
       std::exit(1);
     }
   }
   for (float y : {0.0f, -0.0f}) {
-    if (count_code(tb.thr, y) != bucket_code(tb, y, foff)) {
+    if (count_code(tb.thr, y) != bucket_code(tb, y)) {
       std::fprintf(stderr, "gen_tables: bucket search wrong at signed zero\n");
       std::exit(1);
     }
@@ -196,20 +232,23 @@ void emit_floats(const char* name, const std::vector<float>& v) {
 
 void emit_words(const char* name, const std::vector<uint32_t>& v) {
   std::printf("#define %s { \\\n", name);
-  for (size_t i = 0; i < v.size(); i += 2)
-    std::printf("  0x%08" PRIx32 "u, %" PRIu32 "u%s\n", v[i], v[i + 1], i + 2 < v.size() ? ", \\" : " }");
+  for (size_t i = 0; i < v.size(); i += 4)
+    std::printf("  0x%08" PRIx32 "u, %" PRIu32 "u, 0u, 0u%s\n", v[i], v[i + 1], i + 4 < v.size() ? ", \\" : " }");
 }
 
 }  // namespace
 
 int main() {
-  const Tables q5 = make_tables(32, 192, 96);
-  const Tables q3 = make_tables(8, 192, 96);
-  const Tables kv3 = make_tables(8, 272, 136);
+  const Tables q5 = make_tables(32, 256, 0xff0u);
+  const Tables q3 = make_tables(8, 256, 0xff0u);
+  const Tables kv3 = make_tables(8, 512, 0x1ff0u);
   std::printf("// Generated at build time by gen_tables.cpp: Lloyd-Max tables for N(0,1).\n");
   std::printf("#pragma once\n");
-  std::printf("#define HLWQ_SEARCH_ENTRIES 192\n#define HLWQ_SEARCH_OFFSET 96.0f\n");
-  std::printf("#define HLWQ_KV_SEARCH_ENTRIES 272\n#define HLWQ_KV_SEARCH_OFFSET 136.0f\n");
+  std::printf("#define HLWQ_SEARCH_ENTRIES 256\n#define HLWQ_SEARCH_MASK 0xff0u\n");
+  std::printf("#define HLWQ_SEARCH_OFFSET_5 %af\n#define HLWQ_SEARCH_OFFSET_3 %af\n", (double)q5.offset,
+              (double)q3.offset);
+  std::printf("#define HLWQ_KV_SEARCH_ENTRIES 512\n#define HLWQ_KV_SEARCH_MASK 0x1ff0u\n");
+  std::printf("#define HLWQ_KV_SEARCH_OFFSET %af\n", (double)kv3.offset);
   emit_floats("HLWQ_CENTROIDS_5", q5.cent);
   emit_floats("HLWQ_THRESHOLDS_5", q5.thr);
   emit_words("HLWQ_SEARCH_5", q5.search);

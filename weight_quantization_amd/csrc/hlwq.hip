@@ -22,9 +22,8 @@
 // Rounding.  The file is compiled with -ffp-contract=off: every + and * below
 // is one IEEE round-to-nearest operation in the order written, sqrtf and the
 // division are correctly rounded, and the only fused multiply-adds are the
-// explicit __builtin_fmaf calls whose product is exact (a multiply by 8 or by
-// +-1), so no rounding differs from the operation order documented in
-// include/hlwq.h.
+// explicit __builtin_fmaf calls of the first norm-tree level, so no rounding
+// differs from the operation order documented in include/hlwq.h.
 
 #include <hip/hip_runtime.h>
 
@@ -47,17 +46,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __constant__ float c_cent5[32] = HLWQ_CENTROIDS_5;
 __constant__ float c_cent3[8] = HLWQ_CENTROIDS_3;
-__constant__ uint32_t c_search5[2 * HLWQ_SEARCH_ENTRIES] = HLWQ_SEARCH_5;
-__constant__ uint32_t c_search3[2 * HLWQ_SEARCH_ENTRIES] = HLWQ_SEARCH_3;
-__constant__ uint32_t c_kvsearch3[2 * HLWQ_KV_SEARCH_ENTRIES] = HLWQ_KV_SEARCH_3;
+__constant__ uint32_t c_search5[4 * HLWQ_SEARCH_ENTRIES] = HLWQ_SEARCH_5;
+__constant__ uint32_t c_search3[4 * HLWQ_SEARCH_ENTRIES] = HLWQ_SEARCH_3;
+__constant__ uint32_t c_kvsearch3[4 * HLWQ_KV_SEARCH_ENTRIES] = HLWQ_KV_SEARCH_3;
 
 const float h_cent5[32] = HLWQ_CENTROIDS_5;
 const float h_thr5[31] = HLWQ_THRESHOLDS_5;
 const float h_cent3[8] = HLWQ_CENTROIDS_3;
 const float h_thr3[7] = HLWQ_THRESHOLDS_3;
-const uint32_t h_search5[2 * HLWQ_SEARCH_ENTRIES] = HLWQ_SEARCH_5;
-const uint32_t h_search3[2 * HLWQ_SEARCH_ENTRIES] = HLWQ_SEARCH_3;
-const uint32_t h_kvsearch3[2 * HLWQ_KV_SEARCH_ENTRIES] = HLWQ_KV_SEARCH_3;
+const uint32_t h_search5[4 * HLWQ_SEARCH_ENTRIES] = HLWQ_SEARCH_5;
+const uint32_t h_search3[4 * HLWQ_SEARCH_ENTRIES] = HLWQ_SEARCH_3;
+const uint32_t h_kvsearch3[4 * HLWQ_KV_SEARCH_ENTRIES] = HLWQ_KV_SEARCH_3;
 
 // ---------------------------------------------------------------------------
 // device helpers
@@ -155,13 +154,14 @@ __device__ __forceinline__ void store_block(uint16_t* __restrict__ p, int n, con
   }
 }
 
-// Sum of squares by the adjacent-pair tree: level 0 forms x[2i]^2 + x[2i+1]^2,
-// every further level adds neighbouring partial sums.
+// Sum of squares by the adjacent-pair tree: level 0 forms each pair
+// x[2i]^2 + x[2i+1]^2 with one fused multiply-add (x[2i]^2 exact inside it,
+// x[2i+1]^2 rounded), every further level adds neighbouring partial sums.
 template <int L>
 __device__ __forceinline__ float sumsq_tree(const float (&x)[L]) {
   float s[L / 2];
 #pragma unroll
-  for (int i = 0; i < L / 2; ++i) s[i] = x[2 * i] * x[2 * i] + x[2 * i + 1] * x[2 * i + 1];
+  for (int i = 0; i < L / 2; ++i) s[i] = __builtin_fmaf(x[2 * i], x[2 * i], x[2 * i + 1] * x[2 * i + 1]);
 #pragma unroll
   for (int w = L / 4; w >= 1; w >>= 1)
 #pragma unroll
@@ -196,22 +196,43 @@ __device__ __forceinline__ NormInfo norm_info(float s) {
   return ni;
 }
 
-// y = z * r, code by bucket search, 8 codes of BITS bits per group packed
-// little-endian into W words (code j occupies bits [BITS*j, BITS*j + BITS)).
+// Code of one rotated value: y = z * r, then one read of the bucket table
+// (16-byte entries {threshold, base, -, -}) at byte offset bits(y + offset) &
+// mask, and one compare.  The table generator proves this equals the number
+// of fp32 thresholds strictly below y for every reachable y.
+__device__ __forceinline__ uint32_t code_of(float z, float r, const uint8_t* __restrict__ tab, float offset,
+                                            uint32_t mask) {
+  const float y = z * r;
+  const uint32_t off = __float_as_uint(y + offset) & mask;
+  const uint2 e = *reinterpret_cast<const uint2*>(tab + off);
+  return e.y + ((y > __uint_as_float(e.x)) ? 1u : 0u);
+}
+
+// Encode L values into L * BITS / 32 words: 8 codes of BITS bits per group,
+// little-endian, so code j occupies bits [BITS*j, BITS*j + BITS) of the block's
+// bit string.  Words are built top-down by Horner steps acc = (acc << BITS) +
+// code; a code that straddles two words is computed once, finishes the upper
+// word's bottom bits and starts the lower word.
 template <int BITS, int L>
-__device__ __forceinline__ void encode(const float (&z)[L], float r, const uint2* __restrict__ tab, float offset,
-                                       uint32_t (&w)[L * BITS / 32]) {
+__device__ __forceinline__ void encode(const float (&z)[L], float r, const uint8_t* __restrict__ tab, float offset,
+                                       uint32_t mask, uint32_t (&w)[L * BITS / 32]) {
+  constexpr int W = L * BITS / 32;
+  uint32_t carry = 0;  // straddling code shared with the word below
 #pragma unroll
-  for (int i = 0; i < L * BITS / 32; ++i) w[i] = 0u;
+  for (int wi = W - 1; wi >= 0; --wi) {
+    const int jhi = (32 * wi + 31) / BITS;              // last code touching this word
+    const int jlo = (32 * wi + BITS - 1) / BITS;        // first code starting in this word
+    const int off = BITS * jlo - 32 * wi;               // its bit position (0 .. BITS-1)
+    const bool top_shared = (BITS * jhi + BITS > 32 * (wi + 1)) && (jhi < L);
+    uint32_t acc = top_shared ? carry : code_of(z[jhi], r, tab, offset, mask);
 #pragma unroll
-  for (int j = 0; j < L; ++j) {
-    const float y = z[j] * r;
-    const uint32_t k = static_cast<uint32_t>(__builtin_fmaf(y, 8.0f, offset));
-    const uint2 e = tab[k];
-    const uint32_t code = e.y + ((y > __uint_as_float(e.x)) ? 1u : 0u);
-    const int p = j * BITS;
-    w[p >> 5] |= code << (p & 31);
-    if ((p & 31) + BITS > 32) w[(p >> 5) + 1] |= code >> (32 - (p & 31));
+    for (int j = jhi - 1; j >= jlo; --j) acc = (acc << BITS) + code_of(z[j], r, tab, offset, mask);
+    if (off > 0) {
+      const uint32_t c = code_of(z[jlo - 1], r, tab, offset, mask);
+      acc = (acc << off) + (c >> (BITS - off));
+      carry = c;
+    }
+    w[wi] = acc;
   }
 }
 
@@ -312,6 +333,56 @@ __device__ __forceinline__ void write_staged_block(uint8_t* stage, uint32_t off,
   }
 }
 
+// Fast paths for a full batch whose blocks are all whole and contiguous
+// (64 x 256 bytes): lane l's block sits at bytes [256 l, 256 l + 256) of the
+// batch, so its chunk c lives in slot 16 l + (c ^ (l & 15)) and its LDS
+// address is A_l ^ 16c with A_l = stage + 256 l + 16 (l & 15) (the wave's
+// stage is 256-byte aligned).  In load / store instruction i, lane l handles
+// chunk 64 i + (l ^ (4 (i & 3) + (l >> 4))), i.e. byte offset 1024 i + o[i & 3].
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t*)p));
+}
+__device__ __forceinline__ u32x4 lds_read16(uint32_t a) { return *(const lds_u32x4*)a; }
+__device__ __forceinline__ void lds_write16(uint32_t a, u32x4 v) { *(lds_u32x4*)a = v; }
+
+struct SwzLane {
+  uint32_t o[4];
+};
+__device__ __forceinline__ SwzLane swz_lane(int lane) {
+  SwzLane sl;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) sl.o[k] = 16u * (static_cast<uint32_t>(lane) ^ (4u * k + (static_cast<uint32_t>(lane) >> 4)));
+  return sl;
+}
+
+__device__ __forceinline__ void stage_in_full(const uint8_t* src, uint8_t* stage, const SwzLane& sl) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) __builtin_amdgcn_global_load_lds(src + 1024 * i + sl.o[i & 3], stage + 1024 * i, 16, 0, 0);
+}
+
+__device__ __forceinline__ void read_block_full(uint32_t a, float (&x)[kBlock]) {
+#pragma unroll
+  for (int c = 0; c < 16; ++c) unpack8(lds_read16(a ^ (16u * c)), x, c);
+}
+
+__device__ __forceinline__ void write_block_full(uint32_t a, const uint32_t (&pk)[kBlock / 2]) {
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const u32x4 v = {pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]};
+    lds_write16(a ^ (16u * c), v);
+  }
+}
+
+__device__ __forceinline__ void stage_out_full(uint8_t* dst, uint32_t stage, const SwzLane& sl, int lane) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const u32x4 v = lds_read16(stage + 1024u * i + sl.o[i & 3]);
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + 1024 * i + 16 * lane));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // weight kernels (grouped: up to kMaxGroup matrices per launch)
 //
@@ -328,6 +399,7 @@ struct WeightGroup {
   uint32_t nblocks[kMaxGroup];         // rows * nb
   uint32_t nb[kMaxGroup];              // blocks per row
   int32_t staged[kMaxGroup];           // 1: W rows start 16-byte aligned (in % 8 == 0, W aligned)
+  int32_t whole[kMaxGroup];            // 1: staged and in % 128 == 0 (every block whole)
   int64_t in[kMaxGroup];               // columns
   uint16_t* w[kMaxGroup];
   uint8_t* packed[kMaxGroup];
@@ -365,16 +437,21 @@ __device__ __forceinline__ BatchPos batch_pos(const WeightGroup& g, int d, uint3
 
 template <int BITS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_quantize_kernel(const WeightGroup g) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage_all[kWaves * kStage];
-  __shared__ uint2 tab[HLWQ_SEARCH_ENTRIES];
+  // one LDS array: the bucket table at offset 0 (so table reads need no base
+  // add), then the 256-byte aligned per-wave stages
+  constexpr int kTab = 16 * HLWQ_SEARCH_ENTRIES;
+  __shared__ __attribute__((aligned(256))) uint8_t lds[kTab + kWaves * kStage];
+  uint32_t* tab = reinterpret_cast<uint32_t*>(lds);
+  uint8_t* stage_all = lds + kTab;
   const uint32_t* src_tab = (BITS == 5) ? c_search5 : c_search3;
-  for (int i = threadIdx.x; i < HLWQ_SEARCH_ENTRIES; i += kThreads)
-    tab[i] = make_uint2(src_tab[2 * i], src_tab[2 * i + 1]);
+  for (int i = threadIdx.x; i < 4 * HLWQ_SEARCH_ENTRIES; i += kThreads) tab[i] = src_tab[i];
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint8_t* stage = stage_all + wave * kStage;
+  const SwzLane sl = swz_lane(lane);
+  const uint32_t lane_a = lds_addr(stage) + 256u * lane + 16u * (lane & 15);
   constexpr uint32_t kOut = 16 * BITS;  // packed bytes per block
 
   for (uint32_t b = blockIdx.x * kWaves + wave; b < g.total_batches; b += gridDim.x * kWaves) {
@@ -382,7 +459,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     const BatchPos p = batch_pos(g, d, b, lane);
 
     float x[kBlock];
-    if (g.staged[d]) {
+    if (g.whole[d] && p.nvalid == 64u) {
+      stage_in_full(reinterpret_cast<const uint8_t*>(g.w[d] + static_cast<int64_t>(p.g0) * kBlock), stage, sl);
+      wait_vmem();
+      read_block_full(lane_a, x);
+    } else if (g.staged[d]) {
       const int64_t e0 = first_lane64(p.e);
       const uint32_t off = static_cast<uint32_t>(p.e - e0) * 2u;
       const uint32_t end = __builtin_amdgcn_readlane(off + 2u * p.n, p.nvalid - 1);
@@ -396,7 +477,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     const NormInfo ni = norm_info(sumsq_tree(x));
     fwht(x);
     uint32_t words[4 * BITS];
-    encode<BITS, kBlock>(x, ni.r, tab, HLWQ_SEARCH_OFFSET, words);
+    encode<BITS, kBlock>(x, ni.r, reinterpret_cast<const uint8_t*>(tab),
+                         (BITS == 5) ? HLWQ_SEARCH_OFFSET_5 : HLWQ_SEARCH_OFFSET_3, HLWQ_SEARCH_MASK, words);
 
     // packed output of the batch is contiguous: kOut bytes per block
 #pragma unroll
@@ -411,8 +493,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 
 template <int BITS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_dequantize_kernel(const WeightGroup g) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage_all[kWaves * kStage];
-  __shared__ float cent[1 << BITS];
+  // one LDS array: the centroids at offset 0, then the per-wave stages
+  __shared__ __attribute__((aligned(256))) uint8_t lds[256 + kWaves * kStage];
+  float* cent = reinterpret_cast<float*>(lds);
+  uint8_t* stage_all = lds + 256;
   const float* src_cent = (BITS == 5) ? c_cent5 : c_cent3;
   if (threadIdx.x < (1 << BITS)) cent[threadIdx.x] = src_cent[threadIdx.x];
   __syncthreads();
@@ -420,6 +504,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint8_t* stage = stage_all + wave * kStage;
+  const SwzLane sl = swz_lane(lane);
+  const uint32_t lane_a = lds_addr(stage) + 256u * lane + 16u * (lane & 15);
   constexpr uint32_t kIn = 16 * BITS;  // packed bytes per block
 
   for (uint32_t b = blockIdx.x * kWaves + wave; b < g.total_batches; b += gridDim.x * kWaves) {
@@ -448,7 +534,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
     for (int j = 0; j < kBlock; j += 2) pk[j / 2] = pack_bf16x2(v[j] * scale, v[j + 1] * scale);
 
-    if (g.staged[d]) {
+    if (g.whole[d] && p.nvalid == 64u) {
+      write_block_full(lane_a, pk);
+      stage_out_full(reinterpret_cast<uint8_t*>(g.w[d] + static_cast<int64_t>(p.g0) * kBlock), lds_addr(stage), sl,
+                     lane);
+    } else if (g.staged[d]) {
       const int64_t e0 = first_lane64(p.e);
       const uint32_t off = static_cast<uint32_t>(p.e - e0) * 2u;
       const uint32_t end = __builtin_amdgcn_readlane(off + 2u * p.n, p.nvalid - 1);
@@ -493,23 +583,32 @@ __device__ __forceinline__ KvPos kv_pos(const KvArgs& a, uint32_t b, int lane) {
 }
 
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_kv_quantize_kernel(const KvArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage_all[kWaves * kStage];
-  __shared__ uint2 tab[HLWQ_KV_SEARCH_ENTRIES];
-  for (int i = threadIdx.x; i < HLWQ_KV_SEARCH_ENTRIES; i += kThreads)
-    tab[i] = make_uint2(c_kvsearch3[2 * i], c_kvsearch3[2 * i + 1]);
+  constexpr int kTab = 16 * HLWQ_KV_SEARCH_ENTRIES;
+  __shared__ __attribute__((aligned(256))) uint8_t lds[kTab + kWaves * kStage];
+  uint32_t* tab = reinterpret_cast<uint32_t*>(lds);
+  uint8_t* stage_all = lds + kTab;
+  for (int i = threadIdx.x; i < 4 * HLWQ_KV_SEARCH_ENTRIES; i += kThreads) tab[i] = c_kvsearch3[i];
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint8_t* stage = stage_all + wave * kStage;
+  const SwzLane sl = swz_lane(lane);
+  const uint32_t lane_a = lds_addr(stage) + 256u * lane + 16u * (lane & 15);
 
   for (uint32_t b = blockIdx.x * kWaves + wave; b < a.total_batches; b += gridDim.x * kWaves) {
     const KvPos p = kv_pos(a, b, lane);
     const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv + (static_cast<int64_t>(p.bh) * a.tokens + p.t0) * kKvDim);
-    stage_in<16, true>(src, p.nvalid * 2u * kKvDim, stage, lane);
-    wait_vmem();
     float x[kBlock];
-    read_staged_block(stage, (p.t - p.t0) * 2u * kKvDim + p.half * 2u * kBlock, kBlock, x);
+    if (p.nvalid == 32u) {  // 32 whole vectors: lane l's half-vector is at bytes [256 l, 256 l + 256)
+      stage_in_full(src, stage, sl);
+      wait_vmem();
+      read_block_full(lane_a, x);
+    } else {
+      stage_in<16, true>(src, p.nvalid * 2u * kKvDim, stage, lane);
+      wait_vmem();
+      read_staged_block(stage, (p.t - p.t0) * 2u * kKvDim + p.half * 2u * kBlock, kBlock, x);
+    }
 
     // last tree level joins the two halves (addition commutes, so both lanes agree)
     const float s_half = sumsq_tree(x);
@@ -521,7 +620,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     for (int j = 0; j < kBlock; ++j) x[j] = cross_pair(x[j], sgn);
 
     uint32_t words[12];
-    encode<3, kBlock>(x, ni.r, tab, HLWQ_KV_SEARCH_OFFSET, words);
+    encode<3, kBlock>(x, ni.r, reinterpret_cast<const uint8_t*>(tab), HLWQ_KV_SEARCH_OFFSET, HLWQ_KV_SEARCH_MASK,
+                      words);
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
       const u32x4 v = {words[4 * q], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]};
@@ -534,14 +634,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 }
 
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_kv_dequantize_kernel(const KvArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage_all[kWaves * kStage];
-  __shared__ float cent[8];
+  __shared__ __attribute__((aligned(256))) uint8_t lds[256 + kWaves * kStage];
+  float* cent = reinterpret_cast<float*>(lds);
+  uint8_t* stage_all = lds + 256;
   if (threadIdx.x < 8) cent[threadIdx.x] = c_cent3[threadIdx.x];
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint8_t* stage = stage_all + wave * kStage;
+  const SwzLane sl = swz_lane(lane);
+  const uint32_t lane_a = lds_addr(stage) + 256u * lane + 16u * (lane & 15);
 
   for (uint32_t b = blockIdx.x * kWaves + wave; b < a.total_batches; b += gridDim.x * kWaves) {
     const KvPos p = kv_pos(a, b, lane);
@@ -574,9 +677,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     // lanes past the end of the batch repeat the last vector: identical bytes
     // to the same place, so the write needs no lane mask (a masked region
     // would keep the DPP operands from folding)
-    write_staged_block(stage, (p.t - p.t0) * 2u * kKvDim + p.half * 2u * kBlock, kBlock, pk);
     uint8_t* dst = reinterpret_cast<uint8_t*>(a.kv + (static_cast<int64_t>(p.bh) * a.tokens + p.t0) * kKvDim);
-    stage_out<16, true>(dst, p.nvalid * 2u * kKvDim, stage, lane);
+    if (p.nvalid == 32u) {
+      write_block_full(lane_a, pk);
+      stage_out_full(dst, lds_addr(stage), sl, lane);
+    } else {
+      write_staged_block(stage, (p.t - p.t0) * 2u * kKvDim + p.half * 2u * kBlock, kBlock, pk);
+      stage_out<16, true>(dst, p.nvalid * 2u * kKvDim, stage, lane);
+    }
   }
 }
 
@@ -658,6 +766,7 @@ int run_weight_group(const hlwq_mat_desc* mats, int n, int bits, hipStream_t str
       g.packed[k] = static_cast<uint8_t*>(mats[i].packed);
       g.norms[k] = static_cast<uint16_t*>(mats[i].norms);
       g.staged[k] = (mats[i].in % 8 == 0) && ((reinterpret_cast<uintptr_t>(mats[i].w) & 15u) == 0);
+      g.whole[k] = g.staged[k] && (mats[i].in % kBlock == 0);
       batches += ceil_div(nblk, 64);
       if (batches > 0x7fffffff) return HLWQ_ERR_LIMIT;
     }
@@ -795,21 +904,25 @@ int hlwq_centroids(int bits, float* centroids, float* thresholds) {
   return HLWQ_OK;
 }
 
-int hlwq_search_table(int kind, uint32_t* words, int capacity, float* offset) {
+int hlwq_search_table(int kind, uint32_t* words, int capacity, float* offset, uint32_t* mask) {
   const uint32_t* src;
   int entries;
   float off;
+  uint32_t m;
   switch (kind) {
-    case 0: src = h_search5; entries = HLWQ_SEARCH_ENTRIES; off = HLWQ_SEARCH_OFFSET; break;
-    case 1: src = h_search3; entries = HLWQ_SEARCH_ENTRIES; off = HLWQ_SEARCH_OFFSET; break;
-    case 2: src = h_kvsearch3; entries = HLWQ_KV_SEARCH_ENTRIES; off = HLWQ_KV_SEARCH_OFFSET; break;
+    case 0: src = h_search5; entries = HLWQ_SEARCH_ENTRIES; off = HLWQ_SEARCH_OFFSET_5; m = HLWQ_SEARCH_MASK; break;
+    case 1: src = h_search3; entries = HLWQ_SEARCH_ENTRIES; off = HLWQ_SEARCH_OFFSET_3; m = HLWQ_SEARCH_MASK; break;
+    case 2:
+      src = h_kvsearch3; entries = HLWQ_KV_SEARCH_ENTRIES; off = HLWQ_KV_SEARCH_OFFSET; m = HLWQ_KV_SEARCH_MASK;
+      break;
     default: return HLWQ_ERR_BITS;
   }
   if (words) {
-    const int m = capacity < entries ? capacity : entries;
-    if (m > 0) std::memcpy(words, src, sizeof(uint32_t) * 2 * m);
+    const int n = capacity < entries ? capacity : entries;
+    if (n > 0) std::memcpy(words, src, sizeof(uint32_t) * 4 * n);
   }
   if (offset) *offset = off;
+  if (mask) *mask = m;
   return entries;
 }
 
