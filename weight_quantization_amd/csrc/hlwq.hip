@@ -13,8 +13,10 @@
 // only the last norm level and the last butterfly stage (stride 128) cross
 // lanes, through a DPP quad permutation.
 //
-// Code search.  A rotated value y picks bucket k = (uint32_t) fmaf(y, 8, off)
-// of a small LDS table {threshold, base}; the code is base + (y > threshold).
+// Code search.  A rotated value y picks the entry {threshold, base} of a small
+// LDS table at byte offset bits(y + O) & mask (O puts every reachable y + O in
+// one binade whose low mantissa bits count 1/8-wide buckets); the code is
+// base + (y > threshold).
 // The table is built and proven exact against the plain count at build time
 // (gen_tables.cpp), so the kernels reproduce "number of fp32 thresholds below
 // y" bit for bit with one compare.
