@@ -276,29 +276,51 @@ __device__ __forceinline__ uint32_t swz(uint32_t q) { return q ^ ((q >> 4) & 15u
 // direct-to-LDS loads; the memory clobber keeps LDS reads below it
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Per-lane byte offsets of the swizzled slot pattern: in load / store
+// instruction i, lane l handles chunk 64 i + (l ^ (4 (i & 3) + (l >> 4))),
+// i.e. byte offset 1024 i + o[i & 3] (swz(64 i + l) written out: the row index
+// (64 i + l) >> 4 is 4 i + (l >> 4), whose low 4 bits are 4 (i & 3) + (l >> 4)).
+struct SwzLane {
+  uint32_t o[4];
+};
+
+// Make per-lane address bases opaque at the top of a loop iteration, so the
+// compiler derives the 16 chunk addresses of a batch inside the loop (one add
+// or xor each, or an instruction offset) instead of holding all of them in
+// VGPRs across the whole loop.
+__device__ __forceinline__ void refresh(SwzLane& sl, uint32_t& a) {
+  asm volatile("" : "+v"(sl.o[0]), "+v"(sl.o[1]), "+v"(sl.o[2]), "+v"(sl.o[3]), "+v"(a));
+}
+__device__ __forceinline__ SwzLane swz_lane(int lane) {
+  SwzLane sl;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) sl.o[k] = 16u * (static_cast<uint32_t>(lane) ^ (4u * k + (static_cast<uint32_t>(lane) >> 4)));
+  return sl;
+}
+
 // Stage `bytes` (<= 1024 * NI) of global memory starting at the 16-byte
 // aligned address src: chunk q (16 bytes) lands in slot swz(q) if SWZ, else q.
 // Chunks past `bytes` re-read src and are never consumed.
 template <int NI, bool SWZ>
-__device__ __forceinline__ void stage_in(const uint8_t* src, uint32_t bytes, uint8_t* stage, int lane) {
+__device__ __forceinline__ void stage_in(const uint8_t* src, uint32_t bytes, uint8_t* stage, int lane,
+                                         const SwzLane& sl) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const uint32_t slot = 64u * i + lane;
-    const uint32_t q = SWZ ? swz(slot) : slot;
-    const uint8_t* a = (16u * q < bytes) ? src + 16u * q : src;
-    __builtin_amdgcn_global_load_lds(a, stage + 1024 * i, 16, 0, 0);
+    const uint32_t off = 1024u * i + (SWZ ? sl.o[i & 3] : 16u * lane);
+    __builtin_amdgcn_global_load_lds(src + (off < bytes ? off : 0u), stage + 1024 * i, 16, 0, 0);
   }
 }
 
 // Write back `bytes` of staged output (chunk q in slot swz(q) if SWZ) to dst
 // with 1 KB-contiguous stores.
 template <int NI, bool SWZ>
-__device__ __forceinline__ void stage_out(uint8_t* dst, uint32_t bytes, const uint8_t* stage, int lane) {
+__device__ __forceinline__ void stage_out(uint8_t* dst, uint32_t bytes, const uint8_t* stage, int lane,
+                                          const SwzLane& sl) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const uint32_t q = 64u * i + lane;
     if (16u * q < bytes) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + 16u * (SWZ ? swz(q) : q));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + 1024u * i + (SWZ ? sl.o[i & 3] : 16u * lane));
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + 16u * q));
     }
   }
@@ -348,16 +370,6 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 }
 __device__ __forceinline__ u32x4 lds_read16(uint32_t a) { return *(const lds_u32x4*)a; }
 __device__ __forceinline__ void lds_write16(uint32_t a, u32x4 v) { *(lds_u32x4*)a = v; }
-
-struct SwzLane {
-  uint32_t o[4];
-};
-__device__ __forceinline__ SwzLane swz_lane(int lane) {
-  SwzLane sl;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) sl.o[k] = 16u * (static_cast<uint32_t>(lane) ^ (4u * k + (static_cast<uint32_t>(lane) >> 4)));
-  return sl;
-}
 
 __device__ __forceinline__ void stage_in_full(const uint8_t* src, uint8_t* stage, const SwzLane& sl) {
 #pragma unroll
@@ -415,28 +427,72 @@ __device__ __forceinline__ int group_of(const WeightGroup& g, uint32_t b) {
   return d;
 }
 
-struct BatchPos {
-  uint32_t g0, nvalid, lb;
-  int64_t e;  // element offset of this lane's block in W
-  int n;      // real values in this lane's block
+// Uniform facts about batch b of matrix d.
+struct BatchHead {
+  int d;
+  uint32_t g0, nvalid;
+  bool full;  // 64 whole, contiguous blocks: lane l's block is bytes [256 l, 256 l + 256)
 };
 
-__device__ __forceinline__ BatchPos batch_pos(const WeightGroup& g, int d, uint32_t b, int lane) {
-  BatchPos p;
-  p.g0 = (b - g.batch_start[d]) * 64u;
-  const uint32_t left = g.nblocks[d] - p.g0;
-  p.nvalid = left < 64u ? left : 64u;
-  p.lb = p.g0 + (static_cast<uint32_t>(lane) < p.nvalid ? static_cast<uint32_t>(lane) : p.nvalid - 1);
-  const uint32_t nb = g.nb[d];
+__device__ __forceinline__ BatchHead batch_head(const WeightGroup& g, uint32_t b) {
+  BatchHead h;
+  h.d = group_of(g, b);
+  h.g0 = (b - g.batch_start[h.d]) * 64u;
+  const uint32_t left = g.nblocks[h.d] - h.g0;
+  h.nvalid = left < 64u ? left : 64u;
+  h.full = g.whole[h.d] && h.nvalid == 64u;
+  return h;
+}
+
+// This lane's block: lanes past the end of the batch take the last block.
+struct BatchLane {
+  uint32_t lb;
+  int64_t e;  // element offset of the block in W
+  int n;      // real values in the block
+};
+
+__device__ __forceinline__ BatchLane batch_lane(const WeightGroup& g, const BatchHead& h, int lane) {
+  BatchLane p;
+  p.lb = h.g0 + (static_cast<uint32_t>(lane) < h.nvalid ? static_cast<uint32_t>(lane) : h.nvalid - 1);
+  if (h.full) {
+    p.e = static_cast<int64_t>(p.lb) * kBlock;
+    p.n = kBlock;
+    return p;
+  }
+  const uint32_t nb = g.nb[h.d];
   const uint32_t row = p.lb / nb;
   const uint32_t blk = p.lb - row * nb;
-  const int64_t in = g.in[d];
+  const int64_t in = g.in[h.d];
   const int64_t col = static_cast<int64_t>(blk) * kBlock;
   p.e = static_cast<int64_t>(row) * in + col;
   p.n = static_cast<int>((in - col) < kBlock ? (in - col) : kBlock);
   return p;
 }
 
+// wait for this wave's LDS operations (the stage may be overwritten after it)
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Start the loads of batch b of W into the wave's stage (nothing to do on the
+// element-wise path for unaligned rows).
+__device__ __forceinline__ void quant_issue(const WeightGroup& g, uint32_t b, int lane, uint8_t* stage,
+                                            const SwzLane& sl) {
+  const BatchHead h = batch_head(g, b);
+  if (h.full) {
+    stage_in_full(reinterpret_cast<const uint8_t*>(g.w[h.d] + static_cast<int64_t>(h.g0) * kBlock), stage, sl);
+  } else if (g.staged[h.d]) {
+    const BatchLane p = batch_lane(g, h, lane);
+    const int64_t e0 = first_lane64(p.e);
+    const uint32_t off = static_cast<uint32_t>(p.e - e0) * 2u;
+    const uint32_t end = __builtin_amdgcn_readlane(off + 2u * p.n, h.nvalid - 1);
+    stage_in<16, true>(reinterpret_cast<const uint8_t*>(g.w[h.d] + e0), end, stage, lane, sl);
+  }
+}
+
+// Quantize: each wave loops over its batches; while it computes batch b, the
+// direct-to-LDS loads of its next batch (when that is a full one) are already
+// in flight into the same stage, which has been read into VGPRs by then.  Packed codes
+// (kOut bytes per block, contiguous over the batch) and fp16 norms are stored
+// straight from VGPRs.
 template <int BITS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_quantize_kernel(const WeightGroup g) {
   // one LDS array: the bucket table at offset 0 (so table reads need no base
@@ -452,28 +508,39 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint8_t* stage = stage_all + wave * kStage;
-  const SwzLane sl = swz_lane(lane);
-  const uint32_t lane_a = lds_addr(stage) + 256u * lane + 16u * (lane & 15);
+  SwzLane sl = swz_lane(lane);
+  uint32_t lane_a = lds_addr(stage) + 256u * lane + 16u * (lane & 15);
   constexpr uint32_t kOut = 16 * BITS;  // packed bytes per block
+  const uint32_t step = gridDim.x * kWaves;
 
-  for (uint32_t b = blockIdx.x * kWaves + wave; b < g.total_batches; b += gridDim.x * kWaves) {
-    const int d = group_of(g, b);
-    const BatchPos p = batch_pos(g, d, b, lane);
+  bool in_flight = false;  // loads of batch b already issued (full batches are prefetched)
+  for (uint32_t b = blockIdx.x * kWaves + wave; b < g.total_batches; b += step) {
+    refresh(sl, lane_a);
+    if (!in_flight) quant_issue(g, b, lane, stage, sl);
+    const BatchHead h = batch_head(g, b);
+    const BatchLane p = batch_lane(g, h, lane);
 
     float x[kBlock];
-    if (g.whole[d] && p.nvalid == 64u) {
-      stage_in_full(reinterpret_cast<const uint8_t*>(g.w[d] + static_cast<int64_t>(p.g0) * kBlock), stage, sl);
+    if (h.full) {
       wait_vmem();
       read_block_full(lane_a, x);
-    } else if (g.staged[d]) {
+    } else if (g.staged[h.d]) {
       const int64_t e0 = first_lane64(p.e);
-      const uint32_t off = static_cast<uint32_t>(p.e - e0) * 2u;
-      const uint32_t end = __builtin_amdgcn_readlane(off + 2u * p.n, p.nvalid - 1);
-      stage_in<16, true>(reinterpret_cast<const uint8_t*>(g.w[d] + e0), end, stage, lane);
       wait_vmem();
-      read_staged_block(stage, off, p.n, x);
+      read_staged_block(stage, static_cast<uint32_t>(p.e - e0) * 2u, p.n, x);
     } else {
-      load_block(g.w[d] + p.e, p.n, x);
+      load_block(g.w[h.d] + p.e, p.n, x);
+    }
+    wait_lds();
+    // prefetch the next batch while this one computes, when it is a full one
+    // (a partial batch needs per-lane addresses that would cost VGPRs here)
+    in_flight = false;
+    if (b + step < g.total_batches) {
+      const BatchHead hn = batch_head(g, b + step);
+      if (hn.full) {
+        stage_in_full(reinterpret_cast<const uint8_t*>(g.w[hn.d] + static_cast<int64_t>(hn.g0) * kBlock), stage, sl);
+        in_flight = true;
+      }
     }
 
     const NormInfo ni = norm_info(sumsq_tree(x));
@@ -482,17 +549,22 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     encode<BITS, kBlock>(x, ni.r, reinterpret_cast<const uint8_t*>(tab),
                          (BITS == 5) ? HLWQ_SEARCH_OFFSET_5 : HLWQ_SEARCH_OFFSET_3, HLWQ_SEARCH_MASK, words);
 
-    // packed output of the batch is contiguous: kOut bytes per block
+    // unmasked on purpose: lanes past the end of the batch store the same
+    // bytes as the lane that owns their (clamped) block, and a lane mask here
+    // would keep every code word live until the end of the search
+    u32x4* dst = reinterpret_cast<u32x4*>(g.packed[h.d] + static_cast<size_t>(p.lb) * kOut);
 #pragma unroll
     for (int q = 0; q < BITS; ++q) {
       const u32x4 v = {words[4 * q], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]};
-      *reinterpret_cast<u32x4*>(stage + kOut * lane + 16 * q) = v;
+      dst[q] = v;
     }
-    stage_out<BITS, false>(g.packed[d] + static_cast<size_t>(p.g0) * kOut, p.nvalid * kOut, stage, lane);
-    if (static_cast<uint32_t>(lane) < p.nvalid) g.norms[d][p.lb] = ni.n16;
+    g.norms[h.d][p.lb] = ni.n16;
   }
 }
 
+// Dequantize: the packed codes and norm of the next batch are loaded into
+// VGPRs while the current batch is decoded; bf16 results go through the LDS
+// stage to 1 KB-contiguous stores.
 template <int BITS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_dequantize_kernel(const WeightGroup g) {
   // one LDS array: the centroids at offset 0, then the per-wave stages
@@ -506,28 +578,37 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint8_t* stage = stage_all + wave * kStage;
-  const SwzLane sl = swz_lane(lane);
-  const uint32_t lane_a = lds_addr(stage) + 256u * lane + 16u * (lane & 15);
+  SwzLane sl = swz_lane(lane);
+  uint32_t lane_a = lds_addr(stage) + 256u * lane + 16u * (lane & 15);
   constexpr uint32_t kIn = 16 * BITS;  // packed bytes per block
+  const uint32_t step = gridDim.x * kWaves;
 
-  for (uint32_t b = blockIdx.x * kWaves + wave; b < g.total_batches; b += gridDim.x * kWaves) {
-    const int d = group_of(g, b);
-    const BatchPos p = batch_pos(g, d, b, lane);
+  u32x4 nxt[BITS];
+  uint16_t nxt_n16 = 0;
+  auto fetch = [&](uint32_t bb) {
+    const BatchHead h = batch_head(g, bb);
+    const uint32_t lb = h.g0 + (static_cast<uint32_t>(lane) < h.nvalid ? static_cast<uint32_t>(lane) : h.nvalid - 1);
+    const u32x4* src = reinterpret_cast<const u32x4*>(g.packed[h.d] + static_cast<size_t>(lb) * kIn);
+#pragma unroll
+    for (int q = 0; q < BITS; ++q) nxt[q] = src[q];
+    nxt_n16 = g.norms[h.d][lb];
+  };
 
-    stage_in<BITS, false>(g.packed[d] + static_cast<size_t>(p.g0) * kIn, p.nvalid * kIn, stage, lane);
-    const float scale = f16_value(g.norms[d][p.lb]) * 0x1p-7f;
-    wait_vmem();
-    // lanes past the end of the batch read (and later write) the last block
-    const uint32_t slot = p.lb - p.g0;
+  uint32_t b = blockIdx.x * kWaves + wave;
+  if (b < g.total_batches) fetch(b);
+  for (; b < g.total_batches; b += step) {
+    refresh(sl, lane_a);
+    const BatchHead h = batch_head(g, b);
     uint32_t words[4 * BITS];
 #pragma unroll
     for (int q = 0; q < BITS; ++q) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + kIn * slot + 16 * q);
-      words[4 * q] = v.x;
-      words[4 * q + 1] = v.y;
-      words[4 * q + 2] = v.z;
-      words[4 * q + 3] = v.w;
+      words[4 * q] = nxt[q].x;
+      words[4 * q + 1] = nxt[q].y;
+      words[4 * q + 2] = nxt[q].z;
+      words[4 * q + 3] = nxt[q].w;
     }
+    const float scale = f16_value(nxt_n16) * 0x1p-7f;
+    if (b + step < g.total_batches) fetch(b + step);
 
     float v[kBlock];
     decode<BITS, kBlock>(words, cent, v);
@@ -536,20 +617,24 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
     for (int j = 0; j < kBlock; j += 2) pk[j / 2] = pack_bf16x2(v[j] * scale, v[j + 1] * scale);
 
-    if (g.whole[d] && p.nvalid == 64u) {
+    if (h.full) {
       write_block_full(lane_a, pk);
-      stage_out_full(reinterpret_cast<uint8_t*>(g.w[d] + static_cast<int64_t>(p.g0) * kBlock), lds_addr(stage), sl,
+      stage_out_full(reinterpret_cast<uint8_t*>(g.w[h.d] + static_cast<int64_t>(h.g0) * kBlock), lds_addr(stage), sl,
                      lane);
-    } else if (g.staged[d]) {
-      const int64_t e0 = first_lane64(p.e);
-      const uint32_t off = static_cast<uint32_t>(p.e - e0) * 2u;
-      const uint32_t end = __builtin_amdgcn_readlane(off + 2u * p.n, p.nvalid - 1);
-      // lanes past the end of the batch repeat the last block: identical bytes
-      write_staged_block(stage, off, p.n, pk);
-      stage_out<16, true>(reinterpret_cast<uint8_t*>(g.w[d] + e0), end, stage, lane);
-    } else if (static_cast<uint32_t>(lane) < p.nvalid) {
-      store_block(g.w[d] + p.e, p.n, pk);
+    } else {
+      const BatchLane p = batch_lane(g, h, lane);
+      if (g.staged[h.d]) {
+        const int64_t e0 = first_lane64(p.e);
+        const uint32_t off = static_cast<uint32_t>(p.e - e0) * 2u;
+        const uint32_t end = __builtin_amdgcn_readlane(off + 2u * p.n, h.nvalid - 1);
+        // lanes past the end of the batch repeat the last block: identical bytes
+        write_staged_block(stage, off, p.n, pk);
+        stage_out<16, true>(reinterpret_cast<uint8_t*>(g.w[h.d] + e0), end, stage, lane, sl);
+      } else if (static_cast<uint32_t>(lane) < h.nvalid) {
+        store_block(g.w[h.d] + p.e, p.n, pk);
+      }
     }
+    wait_lds();  // the stage is written again by the next batch
   }
 }
 
@@ -595,10 +680,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint8_t* stage = stage_all + wave * kStage;
-  const SwzLane sl = swz_lane(lane);
-  const uint32_t lane_a = lds_addr(stage) + 256u * lane + 16u * (lane & 15);
+  SwzLane sl = swz_lane(lane);
+  uint32_t lane_a = lds_addr(stage) + 256u * lane + 16u * (lane & 15);
 
   for (uint32_t b = blockIdx.x * kWaves + wave; b < a.total_batches; b += gridDim.x * kWaves) {
+    refresh(sl, lane_a);
     const KvPos p = kv_pos(a, b, lane);
     const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv + (static_cast<int64_t>(p.bh) * a.tokens + p.t0) * kKvDim);
     float x[kBlock];
@@ -607,7 +693,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       wait_vmem();
       read_block_full(lane_a, x);
     } else {
-      stage_in<16, true>(src, p.nvalid * 2u * kKvDim, stage, lane);
+      stage_in<16, true>(src, p.nvalid * 2u * kKvDim, stage, lane, sl);
       wait_vmem();
       read_staged_block(stage, (p.t - p.t0) * 2u * kKvDim + p.half * 2u * kBlock, kBlock, x);
     }
@@ -630,7 +716,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       *reinterpret_cast<u32x4*>(stage + 48 * lane + 16 * q) = v;
     }
     const size_t vec0 = static_cast<size_t>(p.bh) * a.tq + p.t0;
-    stage_out<3, false>(a.packed + vec0 * 96, p.nvalid * 96u, stage, lane);
+    stage_out<3, false>(a.packed + vec0 * 96, p.nvalid * 96u, stage, lane, sl);
     if (p.half == 0 && (static_cast<uint32_t>(lane) >> 1) < p.nvalid) a.norms[vec0 + (lane >> 1)] = ni.n16;
   }
 }
@@ -645,13 +731,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint8_t* stage = stage_all + wave * kStage;
-  const SwzLane sl = swz_lane(lane);
-  const uint32_t lane_a = lds_addr(stage) + 256u * lane + 16u * (lane & 15);
+  SwzLane sl = swz_lane(lane);
+  uint32_t lane_a = lds_addr(stage) + 256u * lane + 16u * (lane & 15);
 
   for (uint32_t b = blockIdx.x * kWaves + wave; b < a.total_batches; b += gridDim.x * kWaves) {
+    refresh(sl, lane_a);
     const KvPos p = kv_pos(a, b, lane);
     const size_t vec0 = static_cast<size_t>(p.bh) * a.tq + p.t0;
-    stage_in<3, false>(a.packed + vec0 * 96, p.nvalid * 96u, stage, lane);
+    stage_in<3, false>(a.packed + vec0 * 96, p.nvalid * 96u, stage, lane, sl);
     const float scale = f16_value(a.norms[vec0 + (p.t - p.t0)]) * 0x1p-8f;
     wait_vmem();
     // lanes past the end of the batch read (and later write) the last vector
@@ -685,7 +772,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       stage_out_full(dst, lds_addr(stage), sl, lane);
     } else {
       write_staged_block(stage, (p.t - p.t0) * 2u * kKvDim + p.half * 2u * kBlock, kBlock, pk);
-      stage_out<16, true>(dst, p.nvalid * 2u * kKvDim, stage, lane);
+      stage_out<16, true>(dst, p.nvalid * 2u * kKvDim, stage, lane, sl);
     }
   }
 }
