@@ -11,7 +11,7 @@ Prints one JSON line: weights/s of quantize + dequantize, with the per-kernel
 HBM roofline (algorithmic bytes / kernel time from HIP events on the launch
 stream) and the CPU oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config NAME]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 1000] [--config NAME]
 """
 from __future__ import annotations
 
@@ -131,8 +131,10 @@ def cpu_baseline(config, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    # the card needs a few hundred milliseconds of sustained load to reach its
+    # steady clocks; 1000 untimed steps is about 0.8 s
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--config", default="qwen36_moe_bank", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

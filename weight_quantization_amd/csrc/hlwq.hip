@@ -427,72 +427,28 @@ __device__ __forceinline__ int group_of(const WeightGroup& g, uint32_t b) {
   return d;
 }
 
-// Uniform facts about batch b of matrix d.
-struct BatchHead {
-  int d;
-  uint32_t g0, nvalid;
-  bool full;  // 64 whole, contiguous blocks: lane l's block is bytes [256 l, 256 l + 256)
+struct BatchPos {
+  uint32_t g0, nvalid, lb;
+  int64_t e;  // element offset of this lane's block in W
+  int n;      // real values in this lane's block
 };
 
-__device__ __forceinline__ BatchHead batch_head(const WeightGroup& g, uint32_t b) {
-  BatchHead h;
-  h.d = group_of(g, b);
-  h.g0 = (b - g.batch_start[h.d]) * 64u;
-  const uint32_t left = g.nblocks[h.d] - h.g0;
-  h.nvalid = left < 64u ? left : 64u;
-  h.full = g.whole[h.d] && h.nvalid == 64u;
-  return h;
-}
-
-// This lane's block: lanes past the end of the batch take the last block.
-struct BatchLane {
-  uint32_t lb;
-  int64_t e;  // element offset of the block in W
-  int n;      // real values in the block
-};
-
-__device__ __forceinline__ BatchLane batch_lane(const WeightGroup& g, const BatchHead& h, int lane) {
-  BatchLane p;
-  p.lb = h.g0 + (static_cast<uint32_t>(lane) < h.nvalid ? static_cast<uint32_t>(lane) : h.nvalid - 1);
-  if (h.full) {
-    p.e = static_cast<int64_t>(p.lb) * kBlock;
-    p.n = kBlock;
-    return p;
-  }
-  const uint32_t nb = g.nb[h.d];
+__device__ __forceinline__ BatchPos batch_pos(const WeightGroup& g, int d, uint32_t b, int lane) {
+  BatchPos p;
+  p.g0 = (b - g.batch_start[d]) * 64u;
+  const uint32_t left = g.nblocks[d] - p.g0;
+  p.nvalid = left < 64u ? left : 64u;
+  p.lb = p.g0 + (static_cast<uint32_t>(lane) < p.nvalid ? static_cast<uint32_t>(lane) : p.nvalid - 1);
+  const uint32_t nb = g.nb[d];
   const uint32_t row = p.lb / nb;
   const uint32_t blk = p.lb - row * nb;
-  const int64_t in = g.in[h.d];
+  const int64_t in = g.in[d];
   const int64_t col = static_cast<int64_t>(blk) * kBlock;
   p.e = static_cast<int64_t>(row) * in + col;
   p.n = static_cast<int>((in - col) < kBlock ? (in - col) : kBlock);
   return p;
 }
 
-// wait for this wave's LDS operations (the stage may be overwritten after it)
-__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// Start the loads of batch b of W into the wave's stage (nothing to do on the
-// element-wise path for unaligned rows).
-__device__ __forceinline__ void quant_issue(const WeightGroup& g, uint32_t b, int lane, uint8_t* stage,
-                                            const SwzLane& sl) {
-  const BatchHead h = batch_head(g, b);
-  if (h.full) {
-    stage_in_full(reinterpret_cast<const uint8_t*>(g.w[h.d] + static_cast<int64_t>(h.g0) * kBlock), stage, sl);
-  } else if (g.staged[h.d]) {
-    const BatchLane p = batch_lane(g, h, lane);
-    const int64_t e0 = first_lane64(p.e);
-    const uint32_t off = static_cast<uint32_t>(p.e - e0) * 2u;
-    const uint32_t end = __builtin_amdgcn_readlane(off + 2u * p.n, h.nvalid - 1);
-    stage_in<16, true>(reinterpret_cast<const uint8_t*>(g.w[h.d] + e0), end, stage, lane, sl);
-  }
-}
-
-// Quantize: each wave loops over its batches; while it computes batch b, the
-// direct-to-LDS loads of its next batch (when that is a full one) are already
-// in flight into the same stage, which has been read into VGPRs by then.  Packed codes
-// (kOut bytes per block, contiguous over the batch) and fp16 norms are stored
-// straight from VGPRs.
 template <int BITS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_quantize_kernel(const WeightGroup g) {
   // one LDS array: the bucket table at offset 0 (so table reads need no base
@@ -511,36 +467,26 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   SwzLane sl = swz_lane(lane);
   uint32_t lane_a = lds_addr(stage) + 256u * lane + 16u * (lane & 15);
   constexpr uint32_t kOut = 16 * BITS;  // packed bytes per block
-  const uint32_t step = gridDim.x * kWaves;
 
-  bool in_flight = false;  // loads of batch b already issued (full batches are prefetched)
-  for (uint32_t b = blockIdx.x * kWaves + wave; b < g.total_batches; b += step) {
+  for (uint32_t b = blockIdx.x * kWaves + wave; b < g.total_batches; b += gridDim.x * kWaves) {
     refresh(sl, lane_a);
-    if (!in_flight) quant_issue(g, b, lane, stage, sl);
-    const BatchHead h = batch_head(g, b);
-    const BatchLane p = batch_lane(g, h, lane);
+    const int d = group_of(g, b);
+    const BatchPos p = batch_pos(g, d, b, lane);
 
     float x[kBlock];
-    if (h.full) {
+    if (g.whole[d] && p.nvalid == 64u) {
+      stage_in_full(reinterpret_cast<const uint8_t*>(g.w[d] + static_cast<int64_t>(p.g0) * kBlock), stage, sl);
       wait_vmem();
       read_block_full(lane_a, x);
-    } else if (g.staged[h.d]) {
+    } else if (g.staged[d]) {
       const int64_t e0 = first_lane64(p.e);
+      const uint32_t off = static_cast<uint32_t>(p.e - e0) * 2u;
+      const uint32_t end = __builtin_amdgcn_readlane(off + 2u * p.n, p.nvalid - 1);
+      stage_in<16, true>(reinterpret_cast<const uint8_t*>(g.w[d] + e0), end, stage, lane, sl);
       wait_vmem();
-      read_staged_block(stage, static_cast<uint32_t>(p.e - e0) * 2u, p.n, x);
+      read_staged_block(stage, off, p.n, x);
     } else {
-      load_block(g.w[h.d] + p.e, p.n, x);
-    }
-    wait_lds();
-    // prefetch the next batch while this one computes, when it is a full one
-    // (a partial batch needs per-lane addresses that would cost VGPRs here)
-    in_flight = false;
-    if (b + step < g.total_batches) {
-      const BatchHead hn = batch_head(g, b + step);
-      if (hn.full) {
-        stage_in_full(reinterpret_cast<const uint8_t*>(g.w[hn.d] + static_cast<int64_t>(hn.g0) * kBlock), stage, sl);
-        in_flight = true;
-      }
+      load_block(g.w[d] + p.e, p.n, x);
     }
 
     const NormInfo ni = norm_info(sumsq_tree(x));
@@ -549,22 +495,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     encode<BITS, kBlock>(x, ni.r, reinterpret_cast<const uint8_t*>(tab),
                          (BITS == 5) ? HLWQ_SEARCH_OFFSET_5 : HLWQ_SEARCH_OFFSET_3, HLWQ_SEARCH_MASK, words);
 
-    // unmasked on purpose: lanes past the end of the batch store the same
-    // bytes as the lane that owns their (clamped) block, and a lane mask here
-    // would keep every code word live until the end of the search
-    u32x4* dst = reinterpret_cast<u32x4*>(g.packed[h.d] + static_cast<size_t>(p.lb) * kOut);
+    // packed output of the batch is contiguous: kOut bytes per block
 #pragma unroll
     for (int q = 0; q < BITS; ++q) {
       const u32x4 v = {words[4 * q], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]};
-      dst[q] = v;
+      *reinterpret_cast<u32x4*>(stage + kOut * lane + 16 * q) = v;
     }
-    g.norms[h.d][p.lb] = ni.n16;
+    stage_out<BITS, false>(g.packed[d] + static_cast<size_t>(p.g0) * kOut, p.nvalid * kOut, stage, lane, sl);
+    if (static_cast<uint32_t>(lane) < p.nvalid) g.norms[d][p.lb] = ni.n16;
   }
 }
 
-// Dequantize: the packed codes and norm of the next batch are loaded into
-// VGPRs while the current batch is decoded; bf16 results go through the LDS
-// stage to 1 KB-contiguous stores.
 template <int BITS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_dequantize_kernel(const WeightGroup g) {
   // one LDS array: the centroids at offset 0, then the per-wave stages
@@ -581,34 +522,26 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   SwzLane sl = swz_lane(lane);
   uint32_t lane_a = lds_addr(stage) + 256u * lane + 16u * (lane & 15);
   constexpr uint32_t kIn = 16 * BITS;  // packed bytes per block
-  const uint32_t step = gridDim.x * kWaves;
 
-  u32x4 nxt[BITS];
-  uint16_t nxt_n16 = 0;
-  auto fetch = [&](uint32_t bb) {
-    const BatchHead h = batch_head(g, bb);
-    const uint32_t lb = h.g0 + (static_cast<uint32_t>(lane) < h.nvalid ? static_cast<uint32_t>(lane) : h.nvalid - 1);
-    const u32x4* src = reinterpret_cast<const u32x4*>(g.packed[h.d] + static_cast<size_t>(lb) * kIn);
-#pragma unroll
-    for (int q = 0; q < BITS; ++q) nxt[q] = src[q];
-    nxt_n16 = g.norms[h.d][lb];
-  };
-
-  uint32_t b = blockIdx.x * kWaves + wave;
-  if (b < g.total_batches) fetch(b);
-  for (; b < g.total_batches; b += step) {
+  for (uint32_t b = blockIdx.x * kWaves + wave; b < g.total_batches; b += gridDim.x * kWaves) {
     refresh(sl, lane_a);
-    const BatchHead h = batch_head(g, b);
+    const int d = group_of(g, b);
+    const BatchPos p = batch_pos(g, d, b, lane);
+
+    stage_in<BITS, false>(g.packed[d] + static_cast<size_t>(p.g0) * kIn, p.nvalid * kIn, stage, lane, sl);
+    const float scale = f16_value(g.norms[d][p.lb]) * 0x1p-7f;
+    wait_vmem();
+    // lanes past the end of the batch read (and later write) the last block
+    const uint32_t slot = p.lb - p.g0;
     uint32_t words[4 * BITS];
 #pragma unroll
     for (int q = 0; q < BITS; ++q) {
-      words[4 * q] = nxt[q].x;
-      words[4 * q + 1] = nxt[q].y;
-      words[4 * q + 2] = nxt[q].z;
-      words[4 * q + 3] = nxt[q].w;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + kIn * slot + 16 * q);
+      words[4 * q] = v.x;
+      words[4 * q + 1] = v.y;
+      words[4 * q + 2] = v.z;
+      words[4 * q + 3] = v.w;
     }
-    const float scale = f16_value(nxt_n16) * 0x1p-7f;
-    if (b + step < g.total_batches) fetch(b + step);
 
     float v[kBlock];
     decode<BITS, kBlock>(words, cent, v);
@@ -617,24 +550,20 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
     for (int j = 0; j < kBlock; j += 2) pk[j / 2] = pack_bf16x2(v[j] * scale, v[j + 1] * scale);
 
-    if (h.full) {
+    if (g.whole[d] && p.nvalid == 64u) {
       write_block_full(lane_a, pk);
-      stage_out_full(reinterpret_cast<uint8_t*>(g.w[h.d] + static_cast<int64_t>(h.g0) * kBlock), lds_addr(stage), sl,
+      stage_out_full(reinterpret_cast<uint8_t*>(g.w[d] + static_cast<int64_t>(p.g0) * kBlock), lds_addr(stage), sl,
                      lane);
-    } else {
-      const BatchLane p = batch_lane(g, h, lane);
-      if (g.staged[h.d]) {
-        const int64_t e0 = first_lane64(p.e);
-        const uint32_t off = static_cast<uint32_t>(p.e - e0) * 2u;
-        const uint32_t end = __builtin_amdgcn_readlane(off + 2u * p.n, h.nvalid - 1);
-        // lanes past the end of the batch repeat the last block: identical bytes
-        write_staged_block(stage, off, p.n, pk);
-        stage_out<16, true>(reinterpret_cast<uint8_t*>(g.w[h.d] + e0), end, stage, lane, sl);
-      } else if (static_cast<uint32_t>(lane) < h.nvalid) {
-        store_block(g.w[h.d] + p.e, p.n, pk);
-      }
+    } else if (g.staged[d]) {
+      const int64_t e0 = first_lane64(p.e);
+      const uint32_t off = static_cast<uint32_t>(p.e - e0) * 2u;
+      const uint32_t end = __builtin_amdgcn_readlane(off + 2u * p.n, p.nvalid - 1);
+      // lanes past the end of the batch repeat the last block: identical bytes
+      write_staged_block(stage, off, p.n, pk);
+      stage_out<16, true>(reinterpret_cast<uint8_t*>(g.w[d] + e0), end, stage, lane, sl);
+    } else if (static_cast<uint32_t>(lane) < p.nvalid) {
+      store_block(g.w[d] + p.e, p.n, pk);
     }
-    wait_lds();  // the stage is written again by the next batch
   }
 }
 
