@@ -1,17 +1,24 @@
-"""HLWQ Q5 quantize + dequantize throughput on one MI355X.
+"""HLWQ quantize + dequantize throughput on one MI355X.
 
-One step = HLWQ Q5 quantize of a whole MoE layer's expert banks followed by the
-dequantize of the result, each as one grouped launch over the two banks: the
-Qwen3.6-35B-A3B-shaped layer, 256 experts, gate_up [256, 1024, 2048] and down
-[256, 2048, 512] bf16 (805,306,368 weights, 2.13 GB of algorithmic traffic per
-direction).  Inputs are seeded synthetic N(0, 0.02^2) values with 0.1 % of each
-expert's entries scaled by 20, resident in HBM before timing starts.
+Default workload (the headline): HLWQ Q5 of one Qwen3.6-35B-A3B-shaped MoE
+layer, 256 experts, gate_up [256, 1024, 2048] and down [256, 2048, 512] bf16
+(805,306,368 weights, 2.13 GB of algorithmic traffic per direction).  One step
+= quantize of both banks (one grouped launch) followed by the dequantize of the
+result (one grouped launch).  Inputs are seeded synthetic N(0, 0.02^2) values
+with 0.1 % of each expert's entries scaled by 20, resident in HBM before timing
+starts; the step's working set (5.8 GB) is far larger than the 256 MB
+Infinity Cache, so every step streams from HBM.
+
+Other workloads (--config) use the same procedure: the Gemma-4-26B-A4B-shaped
+bank, the dense hidden-5120 Linears (Q5 or --bits 3), and the H256 KV cache
+(Q3; two independent caches alternate so the working set exceeds the cache).
 
 Prints one JSON line: weights/s of quantize + dequantize, with the per-kernel
 HBM roofline (algorithmic bytes / kernel time from HIP events on the launch
-stream) and the CPU oracle timed on a bounded sample of the same workload.
+stream), a measured device-to-device copy ceiling, and the CPU oracle timed
+on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 1000] [--config NAME]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 1000] [--config NAME] [--bits 5|3]
 """
 from __future__ import annotations
 
@@ -32,11 +39,16 @@ import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 METRIC = "weights/s and achieved HBM GB/s (% of peak) for Q5 quantize+dequantize"
 
-WORKLOADS = {
-    "qwen36_moe_bank": ("Qwen3.6-35B-A3B-shaped MoE layer, Q5 quantize+dequantize of gate_up "
+DESCRIPTIONS = {
+    "qwen36_moe_bank": ("Qwen3.6-35B-A3B-shaped MoE layer, quantize+dequantize of gate_up "
                         "[256,1024,2048] + down [256,2048,512] bf16, N(0,0.02^2) with 0.1% x20 outliers"),
-    "gemma4_moe_bank": ("Gemma-4-26B-A4B-shaped MoE layer, Q5 quantize+dequantize of gate_up "
+    "gemma4_moe_bank": ("Gemma-4-26B-A4B-shaped MoE layer, quantize+dequantize of gate_up "
                         "[128,1408,2816] + down [128,2816,704] bf16, N(0,0.02^2)"),
+    "dense_5120": ("dense hidden-5120 Linears, quantize+dequantize of [5120,5120] + [17408,5120] + "
+                   "[5120,17408] bf16, Student-t(5)*0.02"),
+    "kv_h256": ("KV cache K and V [1,4,32768,256] bf16 N(0,1), per-head H256, 8 centroids, 3-bit, "
+                "newest 128 tokens kept bf16; quantize+dequantize"),
+    "linear_64x256": "single Linear W[64,256] bf16 N(0,0.02^2), quantize+dequantize (launch-bound)",
 }
 
 
@@ -59,10 +71,10 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def stored_traffic(config):
+def stored_traffic(config, bits):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{config}_q5.txt")
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{config}_q{bits}.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -80,9 +92,9 @@ def stored_traffic(config):
 
 def copy_ceiling(torch, dev, nbytes, reps=10):
     """Device-to-device copy moving the same number of bytes (half read, half
-    written) as one quantize or dequantize launch: the practical HBM ceiling."""
-    n = nbytes // 4  # bytes read = bytes written = nbytes / 2
-    src = torch.empty(n // 2, dtype=torch.float32, device=dev).fill_(1.0)
+    written) as one quantize or dequantize launch: a practical HBM ceiling."""
+    n = max(nbytes // 8, 1 << 20)
+    src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
@@ -101,30 +113,131 @@ def copy_ceiling(torch, dev, nbytes, reps=10):
             "kernel": "torch copy_ (float32 device-to-device)"}
 
 
-def cpu_baseline(config, budget_s=12.0):
-    """The oracle (fp32 canonical tier) on whole expert matrices until the budget is used."""
-    from oracle import hlwq_ref as ref
+def to_device(torch, dev, bits_u16):
+    return torch.from_numpy(np.ascontiguousarray(bits_u16).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def weight_workload(torch, wq, dev, config, bits):
     tensors = list(synth.CONFIGS[config])
-    done_w = 0
-    mats = 0
-    t0 = time.perf_counter()
-    e = 0
-    while time.perf_counter() - t0 < budget_s and e < 256:
-        for t in tensors:
-            w = synth.expert_matrix(config, t, e)
-            packed, n16 = ref.quantize_c(w, 5)
-            ref.dequantize_c(packed, n16, w.shape[1], 5)
-            done_w += w.size
-            mats += 1
-        e += 1
-    dt = time.perf_counter() - t0
+    shapes = []
+    qitems, ditems = [], []
+    for t in tensors:
+        shape = synth.CONFIGS[config][t][1]
+        E, out, n_in = shape if len(shape) == 3 else (1, *shape)
+        shapes.append((E, out, n_in))
+        w = to_device(torch, dev, synth.weight(config, t))
+        nb = -(-n_in // 128)
+        lead = (E, out) if len(shape) == 3 else (out,)
+        p = torch.empty(lead + (nb, 16 * bits), dtype=torch.uint8, device=dev)
+        n = torch.empty(lead + (nb,), dtype=torch.float16, device=dev)
+        qitems.append((w, p, n))
+        ditems.append((torch.empty_like(w), p, n))
     return {
-        "value": done_w / dt,
+        "quantize": lambda: wq.hlwq_quantize_grouped(qitems, bits),
+        "dequantize": lambda: wq.hlwq_dequantize_grouped(ditems, bits),
+        "weights": sum(E * o * i for E, o, i in shapes),
+        "bytes": algorithmic_bytes(shapes, bits),
+        "kernels": (f"hlwq_quantize_kernel<{bits}>", f"hlwq_dequantize_kernel<{bits}>"),
+        "launches": 1,
+        "keep": (qitems, ditems),
+    }
+
+
+def kv_workload(torch, wq, dev, copies=2, n_residual=128):
+    sets = []
+    for c in range(copies):
+        one = []
+        for t in ("K", "V"):
+            host = synth.kv_cache("kv_h256", t, seed=synth.DEFAULT_SEED + c)
+            kv = to_device(torch, dev, host)
+            p, n = wq.hlwq_kv_quantize(kv, n_residual=n_residual)
+            out = kv.clone()
+            one.append((kv, p, n, out))
+        sets.append(one)
+    state = {"i": 0}
+    B, H, T, D = synth.CONFIGS["kv_h256"]["K"][1]
+    tq = T - n_residual
+    elems = 2 * B * H * tq * D
+
+    def quant():
+        for kv, p, n, _ in sets[state["i"] % copies]:
+            wq.hlwq_kv_quantize(kv, n_residual=n_residual, packed=p, norms=n)
+
+    def dequant():
+        for _, p, n, out in sets[state["i"] % copies]:
+            wq.hlwq_kv_dequantize(p, n, out, n_residual=n_residual)
+        state["i"] += 1
+
+    return {
+        "quantize": quant,
+        "dequantize": dequant,
+        "weights": elems,
+        "bytes": elems * 2 + 2 * B * H * tq * (96 + 2),
+        "kernels": ("hlwq_kv_quantize_kernel", "hlwq_kv_dequantize_kernel"),
+        "launches": 2,
+        "keep": sets,
+    }
+
+
+def _oracle_samples(config, bits, worker):
+    """Inputs for one CPU worker: one expert matrix (or 256 rows) of every
+    tensor of the workload, or 1024 tokens of one KV head."""
+    if config == "kv_h256":
+        kv = synth.kv_cache("kv_h256", "K", tokens=1024 + 128)
+        return [kv[:, worker % kv.shape[1]:][:, :1]]
+    samples = []
+    for t in synth.CONFIGS[config]:
+        tid, shape, dist, sigma, ofrac, omult = synth.CONFIGS[config][t]
+        if len(shape) == 3:
+            samples.append(synth.expert_matrix(config, t, worker % shape[0]))
+        else:
+            rng = synth.stream(synth.DEFAULT_SEED, synth.CONFIG_IDS[config], 90 + tid, worker)
+            samples.append(synth.draw(dist, rng, (min(shape[0], 256), shape[1]), sigma, ofrac, omult))
+    return samples
+
+
+def _oracle_worker(args):
+    config, bits, worker, budget_s = args
+    from oracle import hlwq_ref as ref
+    from oracle import lloyd_max
+    lloyd_max.table(bits)  # the codebook is computed once, outside the timing
+    samples = _oracle_samples(config, bits, worker)
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        for w in samples:
+            if config == "kv_h256":
+                p, n = ref.kv_quantize_c(w, n_residual=128)
+                ref.kv_dequantize_c(p, n)
+                done += p.shape[2] * 256
+            else:
+                packed, n16 = ref.quantize_c(w, bits)
+                ref.dequantize_c(packed, n16, w.shape[1], bits)
+                done += w.size
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(config, bits, budget_s=10.0):
+    """The oracle (fp32 canonical tier, plain numpy, untouched) on the host
+    cores: one forked process per core (at most 16), each quantizing and
+    dequantizing its own slice of the workload for `budget_s` seconds.  Inputs
+    are drawn before each worker's clock starts; only oracle calls are timed."""
+    import multiprocessing as mp
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    with mp.get_context("fork").Pool(cores) as pool:
+        res = pool.map(_oracle_worker, [(config, bits, k, budget_s) for k in range(cores)])
+    done = sum(r[0] for r in res)
+    wall = max(r[1] for r in res)
+    what = ("1024 tokens of one KV head" if config == "kv_h256"
+            else "one expert matrix (or 256 rows) of each tensor")
+    return {
+        "value": done / wall,
         "unit": "weights/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"{mats} expert matrices ({e} experts x {len(tensors)} banks) of {config}, "
-                  f"Q5 quantize+dequantize, one process, {dt:.1f} s",
+        "sample": f"{cores} processes x {budget_s:.0f} s, each on {what} of {config} (Q{bits} quantize+"
+                  f"dequantize, repeated): {done} weights in {wall:.1f} s; "
+                  f"{done / wall / cores:.3g} weights/s per core",
     }
 
 
@@ -133,15 +246,25 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     # the card needs a few hundred milliseconds of sustained load to reach its
-    # steady clocks; 1000 untimed steps is about 0.8 s
+    # steady clocks; 1000 untimed steps is about 0.8 s on the default workload
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--config", default="qwen36_moe_bank", choices=sorted(WORKLOADS))
+    ap.add_argument("--config", default="qwen36_moe_bank", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--bits", type=int, default=None, choices=(5, 3))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the HLWQ path shards by expert / row with no exchange, "
               "and multi-GPU runs are not part of this build; use --gpus 1", file=sys.stderr)
         sys.exit(2)
+    config = args.config
+    bits = args.bits if args.bits is not None else (3 if config == "kv_h256" else 5)
+    if config == "kv_h256" and bits != 3:
+        ap.error("the KV-cache path is 3-bit")
+    print(f"[bench] timing the CPU oracle ({config}, Q{bits})", file=sys.stderr, flush=True)
+
+    # the CPU oracle runs first, in forked processes, before this process
+    # touches the GPU
+    cpu = None if args.no_cpu_baseline else cpu_baseline(config, bits)
 
     import torch
     import weight_quantization_amd as wq
@@ -149,29 +272,19 @@ def main():
     wq.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    config = args.config
-    tensors = list(synth.CONFIGS[config])
-    shapes = [synth.CONFIGS[config][t][1] for t in tensors]
-    weights = sum(E * o * i for E, o, i in shapes)
-    bytes_dir = algorithmic_bytes(shapes)
 
-    print(f"[bench] generating {config} ({weights} weights)", file=sys.stderr, flush=True)
-    qitems, ditems = [], []
-    for t, (E, out, n_in) in zip(tensors, shapes):
-        host = synth.weight(config, t)
-        w = torch.from_numpy(host.view(np.int16)).view(torch.bfloat16).to(dev)
-        del host
-        nb = -(-n_in // 128)
-        p = torch.empty((E, out, nb, 80), dtype=torch.uint8, device=dev)
-        n = torch.empty((E, out, nb), dtype=torch.float16, device=dev)
-        qitems.append((w, p, n))
-        ditems.append((torch.empty_like(w), p, n))
+    print(f"[bench] generating {config}", file=sys.stderr, flush=True)
+    if config == "kv_h256":
+        wl = kv_workload(torch, wq, dev)
+    else:
+        wl = weight_workload(torch, wq, dev, config, bits)
+    weights, bytes_dir, launches = wl["weights"], wl["bytes"], wl["launches"]
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
-        wq.hlwq_quantize_grouped(qitems, 5)
-        wq.hlwq_dequantize_grouped(ditems, 5)
+        wl["quantize"]()
+        wl["dequantize"]()
     torch.cuda.synchronize()
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -180,9 +293,9 @@ def main():
     t0 = time.perf_counter()
     for s in range(args.steps):
         ev[s][0].record(stream)
-        wq.hlwq_quantize_grouped(qitems, 5)
+        wl["quantize"]()
         ev[s][1].record(stream)
-        wq.hlwq_dequantize_grouped(ditems, 5)
+        wl["dequantize"]()
         ev[s][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -192,21 +305,23 @@ def main():
 
     q_gbs = bytes_dir / (q_ms.mean() * 1e-3) / 1e9
     d_gbs = bytes_dir / (d_ms.mean() * 1e-3) / 1e9
-    dominant = "quantize" if q_ms.mean() >= d_ms.mean() else "dequantize"
+    dom = 0 if q_ms.mean() >= d_ms.mean() else 1
     dom_ms = max(q_ms.mean(), d_ms.mean())
     achieved = bytes_dir / (dom_ms * 1e-3) / 1e9
-    traffic = stored_traffic(config)
+    traffic = stored_traffic(config, bits)
     roofline = {
         "bound": "hbm",
-        "kernel": f"hlwq_{dominant}_kernel<5> (grouped launch over both banks)",
+        "kernel": wl["kernels"][dom] + ("" if launches == 1 else f" ({launches} launches per step)"),
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": (None if traffic is None else traffic[f"{dominant}_bytes_per_launch"]),
-        "algorithmic_bytes_per_launch": bytes_dir,
-        "avg_launch_ms": round(dom_ms, 4),
+        "traffic": (None if traffic is None else
+                    traffic["quantize_bytes_per_launch" if dom == 0 else "dequantize_bytes_per_launch"]),
+        "algorithmic_bytes_per_launch": bytes_dir // launches,
+        "avg_launch_ms": round(dom_ms / launches, 4),
     }
+    step_gbs = 2 * bytes_dir / (ms_per_step * 1e-3) / 1e9
     result = {
         "metric": METRIC,
         "value": weights / (ms_per_step * 1e-3),
@@ -220,23 +335,22 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": WORKLOADS[config], "weights": weights, "bits": 5, "block": 128,
-                   "experts": shapes[0][0]},
-        "hbm_gbs": round(2 * bytes_dir / (ms_per_step * 1e-3) / 1e9, 1),
-        "hbm_frac": round(2 * bytes_dir / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "config": {"workload": DESCRIPTIONS[config], "name": config, "weights": weights, "bits": bits,
+                   "block": 256 if config == "kv_h256" else 128},
+        "hbm_gbs": round(step_gbs, 1),
+        "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "quantize": {"ms": round(float(q_ms.mean()), 4), "ms_min": round(float(q_ms.min()), 4),
                      "gbs": round(q_gbs, 1), "weights_per_s": weights / (q_ms.mean() * 1e-3)},
         "dequantize": {"ms": round(float(d_ms.mean()), 4), "ms_min": round(float(d_ms.min()), 4),
                        "gbs": round(d_gbs, 1), "weights_per_s": weights / (d_ms.mean() * 1e-3)},
         "roofline": roofline,
     }
-    result["copy_ceiling"] = copy_ceiling(torch, dev, bytes_dir)
-    result["copy_frac"] = round(2 * bytes_dir / (ms_per_step * 1e-3) / 1e9 / result["copy_ceiling"]["gbs"], 4)
-    del qitems, ditems
+    result["copy_ceiling"] = copy_ceiling(torch, dev, bytes_dir // launches)
+    result["copy_frac"] = round(step_gbs / result["copy_ceiling"]["gbs"], 4)
+    del wl
     torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(config)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

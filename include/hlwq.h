@@ -147,9 +147,10 @@ int hlwq_centroids(int bits, float* centroids, float* thresholds);
 
 /* Copy the bucket table the kernels use to find a code with one compare.
  * For a rotated value y the kernels form u = y + offset in fp32 and read the
- * 16-byte entry at byte offset (bits(u) & mask) of the table: {threshold bits
- * (fp32, +inf if the bucket holds none), count of thresholds below the bucket,
- * 0, 0}; the code is count + (y > threshold).  kind 0: Q5 weights, 1: Q3
+ * 8 bytes at byte offset (bits(u) & mask) of the table, i.e. one of the two
+ * identical halves of a 16-byte entry {threshold bits (fp32, +inf if the
+ * bucket holds none), count of thresholds below the bucket} x 2; the code is
+ * count + (y > threshold).  kind 0: Q5 weights, 1: Q3
  * weights, 2: Q3 KV.  Copies at most `capacity` entries (4 * capacity
  * uint32) into `words` (may be NULL), stores the offset and mask, and returns
  * the entry count, or a negative status.  Host-only; exposed so the table can

@@ -26,6 +26,7 @@ the index of the nearest fp32 centroid, ties going to the lower index.
 """
 from __future__ import annotations
 
+import functools
 import math
 
 import numpy as np
@@ -89,7 +90,13 @@ def thresholds_f32(c32: np.ndarray) -> np.ndarray:
     return b
 
 
-def table(bits: int):
-    """(c32, b32) for a 2**bits-level codebook."""
+@functools.lru_cache(maxsize=None)
+def _table(bits: int):
     c32 = centroids_f32(1 << bits)
     return c32, thresholds_f32(c32)
+
+
+def table(bits: int):
+    """(c32, b32) for a 2**bits-level codebook (fresh copies of a cached table)."""
+    c32, b32 = _table(bits)
+    return c32.copy(), b32.copy()

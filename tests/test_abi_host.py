@@ -42,9 +42,10 @@ def _bucket_codes(table, offset, mask, y):
     # fp32 rounding of it matters, so rounding it to fp32 reproduces the add.
     y = np.asarray(y, np.float32)
     u = (y.astype(np.float64) + np.float64(offset)).astype(np.float32)
-    k = (u.view(np.uint32) & np.uint32(mask)) >> 4
-    thr = table[k, 0].view(np.float32)
-    return table[k, 1].astype(np.int64) + (y > thr)
+    off = (u.view(np.uint32) & np.uint32(mask)) >> 2   # word index of the 8 bytes read
+    flat = table.reshape(-1)
+    thr = flat[off].view(np.float32)
+    return flat[off + 1].astype(np.int64) + (y > thr)
 
 
 @pytest.mark.parametrize("kind,bits,limit", [(0, 5, 11.32), (1, 3, 11.32), (2, 3, 16.0)])
@@ -55,6 +56,7 @@ def test_bucket_table_reproduces_threshold_count(kind, bits, limit):
     table, offset, mask = wq.hlwq_search_table(kind)
     _, b32 = lm.table(bits)
     assert table.shape[0] == (mask >> 4) + 1
+    assert np.array_equal(table[:, :2], table[:, 2:])  # two identical copies per entry
     half = table.shape[0] / 16.0
     assert limit < half - 0.25
     edges = (98304.0 + np.arange(table.shape[0] + 1) / 8.0 - offset)

@@ -117,7 +117,7 @@ def hlwq_centroids(bits: int):
 
 
 def hlwq_search_table(kind: int):
-    """(entries uint32[n, 4] = {threshold bits, base, 0, 0}, offset, mask) of a bucket table."""
+    """(entries uint32[n, 4] = {threshold bits, base} x 2, offset, mask) of a bucket table."""
     lib = load_library()
     off = ctypes.c_float()
     mask = ctypes.c_uint32()

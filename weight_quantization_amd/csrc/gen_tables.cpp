@@ -12,10 +12,12 @@
 //
 // Bucket search.  For a rotated value y the kernels form, in fp32,
 //   u = y + O            (one rounding; O lies in [2^16, 2^17), ulp 1/128)
-// and read the entry at LDS byte offset  bits(u) & MASK.  Every u the kernels
-// can produce lies in one aligned window of that binade in which the masked
-// mantissa bits count buckets of width 1/8 (16 ulps), so the masked bits are
-// the byte offset of a 16-byte entry with no shift.  The entry is
+// and read 8 bytes at LDS byte offset  bits(u) & MASK.  Every u the kernels
+// can produce lies in one aligned window of that binade in which mantissa
+// bits 4 and up count buckets of width 1/8 (16 ulps), so the masked bits are
+// the byte offset of a 16-byte entry with no shift; bit 3 of u (which half of
+// its bucket y fell in) picks one of two identical 8-byte copies inside the
+// entry, which spreads the reads of a wave over twice as many LDS banks.  The entry is
 // {threshold t_k or +inf, base_k} and the code is base_k + (y > t_k).
 // Buckets are narrower than the smallest gap between thresholds, so each holds
 // at most one threshold; base_k counts the thresholds below the bucket.  The
@@ -30,8 +32,8 @@
 //
 // |y| <= sqrt(128) * (1 + 2e-6) for every finite 128-block (Cauchy-Schwarz on
 // the unit-norm rotated block), inside the 32-wide window of the weight
-// tables (256 entries, MASK 0xff0); 256-wide KV vectors reach |y| <= 16, so
-// their table spans a 64-wide window (512 entries, MASK 0x1ff0).
+// tables (256 entries, MASK 0xff8); 256-wide KV vectors reach |y| <= 16, so
+// their table spans a 64-wide window (512 entries, MASK 0x1ff8).
 
 #include <cinttypes>
 #include <cmath>
@@ -98,7 +100,7 @@ uint32_t f2u(float f) {
 struct Tables {
   int K;
   std::vector<float> cent, thr;
-  std::vector<uint32_t> search;  // 16-byte entries {threshold bits, base, 0, 0}
+  std::vector<uint32_t> search;  // 16-byte entries {threshold bits, base} x 2
   float offset = 0.0f;           // O
   uint32_t mask = 0;             // byte-offset mask of bits(u)
 };
@@ -116,10 +118,10 @@ uint32_t bucket_code(const Tables& tb, float y) {
   const float u = y + tb.offset;  // one fp32 rounding, as on the device
   uint32_t bits;
   std::memcpy(&bits, &u, 4);
-  const uint32_t k = (bits & tb.mask) >> 4;
+  const uint32_t off = (bits & tb.mask) >> 2;  // word index of the 8-byte copy read
   float t;
-  std::memcpy(&t, &tb.search[4 * k], 4);
-  return tb.search[4 * k + 1] + ((y > t) ? 1u : 0u);
+  std::memcpy(&t, &tb.search[off], 4);
+  return tb.search[off + 1] + ((y > t) ? 1u : 0u);
 }
 
 // y-interval [lo, hi) of bucket k for window offset O
@@ -181,8 +183,8 @@ Tables make_tables(int K, int entries, uint32_t mask) {
     }
     tb.search.push_back(f2u(t_in));
     tb.search.push_back(base);
-    tb.search.push_back(0u);
-    tb.search.push_back(0u);
+    tb.search.push_back(f2u(t_in));
+    tb.search.push_back(base);
   }
   // brute-force verification over the reachable range |y| < half - 1/8
   const float ymax = (float)(half - 0.25);
@@ -233,21 +235,22 @@ void emit_floats(const char* name, const std::vector<float>& v) {
 void emit_words(const char* name, const std::vector<uint32_t>& v) {
   std::printf("#define %s { \\\n", name);
   for (size_t i = 0; i < v.size(); i += 4)
-    std::printf("  0x%08" PRIx32 "u, %" PRIu32 "u, 0u, 0u%s\n", v[i], v[i + 1], i + 4 < v.size() ? ", \\" : " }");
+    std::printf("  0x%08" PRIx32 "u, %" PRIu32 "u, 0x%08" PRIx32 "u, %" PRIu32 "u%s\n", v[i], v[i + 1], v[i + 2],
+                v[i + 3], i + 4 < v.size() ? ", \\" : " }");
 }
 
 }  // namespace
 
 int main() {
-  const Tables q5 = make_tables(32, 256, 0xff0u);
-  const Tables q3 = make_tables(8, 256, 0xff0u);
-  const Tables kv3 = make_tables(8, 512, 0x1ff0u);
+  const Tables q5 = make_tables(32, 256, 0xff8u);
+  const Tables q3 = make_tables(8, 256, 0xff8u);
+  const Tables kv3 = make_tables(8, 512, 0x1ff8u);
   std::printf("// Generated at build time by gen_tables.cpp: Lloyd-Max tables for N(0,1).\n");
   std::printf("#pragma once\n");
-  std::printf("#define HLWQ_SEARCH_ENTRIES 256\n#define HLWQ_SEARCH_MASK 0xff0u\n");
+  std::printf("#define HLWQ_SEARCH_ENTRIES 256\n#define HLWQ_SEARCH_MASK 0xff8u\n");
   std::printf("#define HLWQ_SEARCH_OFFSET_5 %af\n#define HLWQ_SEARCH_OFFSET_3 %af\n", (double)q5.offset,
               (double)q3.offset);
-  std::printf("#define HLWQ_KV_SEARCH_ENTRIES 512\n#define HLWQ_KV_SEARCH_MASK 0x1ff0u\n");
+  std::printf("#define HLWQ_KV_SEARCH_ENTRIES 512\n#define HLWQ_KV_SEARCH_MASK 0x1ff8u\n");
   std::printf("#define HLWQ_KV_SEARCH_OFFSET %af\n", (double)kv3.offset);
   emit_floats("HLWQ_CENTROIDS_5", q5.cent);
   emit_floats("HLWQ_THRESHOLDS_5", q5.thr);
