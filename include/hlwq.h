@@ -145,17 +145,20 @@ size_t hlwq_norm_count(int64_t rows, int64_t in, int block);
  * 2^bits - 1 decision thresholds.  bits = 5 or 3.  Host-only, no GPU needed. */
 int hlwq_centroids(int bits, float* centroids, float* thresholds);
 
-/* Copy the bucket table the kernels use to find a code with one compare.
- * For a rotated value y the kernels form u = y + offset in fp32 and read the
- * 8 bytes at byte offset (bits(u) & mask) of the table, i.e. one of the two
- * identical halves of a 16-byte entry {threshold bits (fp32, +inf if the
- * bucket holds none), count of thresholds below the bucket} x 2; the code is
- * count + (y > threshold).  kind 0: Q5 weights, 1: Q3
- * weights, 2: Q3 KV.  Copies at most `capacity` entries (4 * capacity
- * uint32) into `words` (may be NULL), stores the offset and mask, and returns
- * the entry count, or a negative status.  Host-only; exposed so the table can
- * be verified. */
-int hlwq_search_table(int kind, uint32_t* words, int capacity, float* offset, uint32_t* mask);
+/* Copy the two tables the kernels use to find a code with one compare.  For
+ * a rotated value y the kernels form u = fma(y, scale, bias) in fp32, with
+ * scale = 2^-146 and bias the denormal whose bit pattern is `bias_bits`; for
+ * every value a finite input can produce, u is a denormal, so its bit pattern
+ * k = RN(8 y) + bias_bits indexes the bucket table.  Byte k of that table is 8
+ * times the number of thresholds below the 1/8-wide bucket k; at that byte
+ * offset the entry table holds {fp32 bits of threshold b (+inf for the last),
+ * b}, and the code is b + (y > threshold b).  kind 0: Q5 weights, 1: Q3
+ * weights, 2: Q3 KV.  Copies at most `capacity` bucket bytes into `buckets`
+ * and the 2 * 2^bits entry words into `entries` (either may be NULL), stores
+ * scale and bias_bits, and returns the bucket count, or a negative status.
+ * Host-only; exposed so the tables can be verified. */
+int hlwq_search_table(int kind, uint8_t* buckets, int capacity, uint32_t* entries, float* scale,
+                      uint32_t* bias_bits);
 
 /* Static, human-readable text for a status code. */
 const char* hlwq_status_string(int status);

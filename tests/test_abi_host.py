@@ -37,29 +37,33 @@ def test_codebook_matches_oracle(bits):
     assert np.array_equal(t.view(np.uint32), ot.view(np.uint32))
 
 
-def _bucket_codes(table, offset, mask, y):
-    # u = y + offset with one fp32 rounding: the fp64 sum is exact whenever the
-    # fp32 rounding of it matters, so rounding it to fp32 reproduces the add.
+def _bucket_codes(buckets, entries, scale, bias, y):
+    # u = fma(y, 2^-146, bias) lands on the denormal grid (spacing 2^-149), so
+    # its bit pattern is the integer RN(8 y + bias), ties to even; 8 y + bias is
+    # exact in fp64 whenever the rounding can be a tie, so np.rint reproduces it.
+    assert scale == 2.0 ** -146
     y = np.asarray(y, np.float32)
-    u = (y.astype(np.float64) + np.float64(offset)).astype(np.float32)
-    off = (u.view(np.uint32) & np.uint32(mask)) >> 2   # word index of the 8 bytes read
-    flat = table.reshape(-1)
-    thr = flat[off].view(np.float32)
-    return flat[off + 1].astype(np.int64) + (y > thr)
+    k = np.rint(8.0 * y.astype(np.float64) + bias).astype(np.int64)
+    assert k.min() >= 0 and k.max() < buckets.size
+    e = buckets[k].astype(np.int64)
+    assert np.all(e % 8 == 0)
+    thr = entries[e // 8, 0].view(np.float32)
+    return entries[e // 8, 1].astype(np.int64) + (y > thr)
 
 
-@pytest.mark.parametrize("kind,bits,limit", [(0, 5, 11.32), (1, 3, 11.32), (2, 3, 16.0)])
+@pytest.mark.parametrize("kind,bits,limit", [(0, 5, 127.875), (1, 3, 127.875), (2, 3, 255.875)])
 def test_bucket_table_reproduces_threshold_count(kind, bits, limit):
-    # The kernels find codes with one table read and one compare; on every
+    # The kernels find codes with two table reads and one compare; on every
     # fp32 value near a threshold or a bucket edge, and on a dense sweep of the
-    # reachable range, that must equal the oracle's threshold count.
-    table, offset, mask = wq.hlwq_search_table(kind)
+    # reachable range (|y| < 112 for weights, < 222 for KV vectors, even for
+    # blocks whose squares underflow), that must equal the oracle's count.
+    buckets, entries, scale, bias = wq.hlwq_search_table(kind)
     _, b32 = lm.table(bits)
-    assert table.shape[0] == (mask >> 4) + 1
-    assert np.array_equal(table[:, :2], table[:, 2:])  # two identical copies per entry
-    half = table.shape[0] / 16.0
-    assert limit < half - 0.25
-    edges = (98304.0 + np.arange(table.shape[0] + 1) / 8.0 - offset)
+    K = 1 << bits
+    assert entries.shape == (K, 2) and np.array_equal(entries[:, 1], np.arange(K))
+    assert np.array_equal(entries[:-1, 0].view(np.float32), b32) and np.isinf(entries[-1, 0].view(np.float32))
+    assert buckets.size == 2 * bias and limit < bias / 8.0
+    edges = (np.arange(buckets.size + 1) - bias - 0.5) / 8.0
     probes = np.concatenate([b32, edges]).astype(np.float32)
     steps = np.arange(-4096, 4097, dtype=np.int64)
     near = []
@@ -69,9 +73,10 @@ def test_bucket_table_reproduces_threshold_count(kind, bits, limit):
         near.append(np.copysign(v, p) if p != 0 else np.concatenate([v, -v]))
     rng = np.random.default_rng(0)
     y = np.concatenate(near + [np.linspace(-limit, limit, 2_000_001, dtype=np.float32),
-                               rng.standard_normal(200_000).astype(np.float32), np.float32([0.0, -0.0])])
+                               rng.standard_normal(200_000).astype(np.float32),
+                               np.float32([0.0, -0.0, 2.0 ** -149, -2.0 ** -149])])
     y = y[np.abs(y) <= limit]
-    assert np.array_equal(_bucket_codes(table, offset, mask, y), ref.codes_from_y(y, b32))
+    assert np.array_equal(_bucket_codes(buckets, entries, scale, bias, y), ref.codes_from_y(y, b32))
 
 
 def test_size_helpers():

@@ -125,7 +125,17 @@ def _special_rows():
     rows.append(neg0)
     alt = np.where(np.arange(256) % 2 == 0, 1.0, -1.0).astype(np.float32)
     rows.append(alt)
+    rows.append(np.concatenate([underflow_vector(128), underflow_vector(128)[::-1]]))
     return f(np.stack(rows))
+
+
+def underflow_vector(n):
+    """One entry whose square rounds up to 2^-149 and n - 1 whose squares round
+    to 0: the computed norm is far below the exact one, so |y| reaches about
+    0.7 n, beyond sqrt(n)."""
+    v = np.full(n, np.float32(255 / 256 * 2.0 ** -75))
+    v[0] = np.float32(1.5 * 2.0 ** -75)
+    return v
 
 
 @pytest.mark.parametrize("bits", [5, 3])
@@ -192,6 +202,23 @@ def test_kv_cache_small(wq, shape):
     got = bf16_bits(out)
     assert np.array_equal(got[:, :, :tq], ref.kv_dequantize_c(op, on))
     assert np.all(got[:, :, tq:] == 0x3F80), "residual window must stay untouched"
+
+
+def test_kv_cache_underflow_vectors(wq):
+    f = synth.f32_to_bf16_bits
+    kv = synth.random_bf16((1, 2, 200, 256), seed=77, sigma=1.0)
+    kv[0, 0, 3] = f(underflow_vector(256))
+    kv[0, 1, 71] = f(-underflow_vector(256)[::-1])
+    _say("kv underflow vectors")
+    dev = to_dev(kv)
+    packed, norms = wq.hlwq_kv_quantize(dev, n_residual=128)
+    out = torch.empty_like(dev)
+    wq.hlwq_kv_dequantize(packed, norms, out, n_residual=128)
+    torch.cuda.synchronize()
+    op, on = ref.kv_quantize_c(kv, n_residual=128)
+    assert np.array_equal(packed.cpu().numpy(), op)
+    assert np.array_equal(f16_bits(norms), on.view(np.uint16))
+    assert np.array_equal(bf16_bits(out)[:, :, :72], ref.kv_dequantize_c(op, on))
 
 
 # --------------------------------------------------------------------------

@@ -183,3 +183,19 @@ def test_linear_golden_regression():
     assert bytes(n16.view(np.uint16).astype("<u2").ravel().view(np.uint8)).hex() == g["norms_hex"]
     out = ref.dequantize_c(packed, n16, 256, 5)
     assert bytes(out.astype("<u2").ravel().view(np.uint8)).hex() == g["dequant_hex"]
+
+
+def test_underflowing_squares_reach():
+    # Squares below 2^-150 vanish from the fp32 norm sum, so a block of such
+    # values next to one larger value gets a norm far below its exact one and
+    # rotated values far beyond sqrt(L); the code is still the nearest centroid
+    # (the top one).  The bound |y| < sqrt(L * (1 + R / 2)), R the roundings of
+    # the norm sum, is what sizes the kernels' search tables.
+    for L, bits, rounds in ((128, 5, 191), (256, 3, 383)):
+        v = np.full(L, np.float32(255 / 256 * 2.0 ** -75))
+        v[0] = np.float32(1.5 * 2.0 ** -75)
+        codes, n, _, y = ref.quantize_vectors_c(v[None], bits)
+        assert n[0] == np.float32(2.0 ** -74.5)            # only the first square survives
+        assert abs(float(y[0, 0]) - (1.5 + (L - 1) * 255 / 256) * 2.0 ** -0.5) < 1e-3 * L
+        assert np.abs(y).max() < math.sqrt(L * (1 + rounds / 2))
+        assert codes[0, 0] == (1 << bits) - 1

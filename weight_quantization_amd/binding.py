@@ -54,8 +54,8 @@ _SIGNATURES = {
     "hlwq_kv_dequantize": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _i64, _vp, _vp]),
     "hlwq_packed_bytes": (ctypes.c_size_t, [_i64, _i64, _int, _int]),
     "hlwq_norm_count": (ctypes.c_size_t, [_i64, _i64, _int]),
-    "hlwq_search_table": (_int, [_int, ctypes.POINTER(ctypes.c_uint32), _int, ctypes.POINTER(ctypes.c_float),
-                                 ctypes.POINTER(ctypes.c_uint32)]),
+    "hlwq_search_table": (_int, [_int, ctypes.POINTER(ctypes.c_uint8), _int, ctypes.POINTER(ctypes.c_uint32),
+                                 ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_uint32)]),
     "hlwq_status_string": (ctypes.c_char_p, [_int]),
 }
 _SIGNATURES["hlwq_centroids"] = (_int, [_int, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)])
@@ -117,16 +117,19 @@ def hlwq_centroids(bits: int):
 
 
 def hlwq_search_table(kind: int):
-    """(entries uint32[n, 4] = {threshold bits, base} x 2, offset, mask) of a bucket table."""
+    """(bucket bytes uint8[n], entries uint32[K, 2] = {threshold bits, b}, scale, bias bits)."""
     lib = load_library()
-    off = ctypes.c_float()
-    mask = ctypes.c_uint32()
-    n = lib.hlwq_search_table(kind, None, 0, ctypes.byref(off), ctypes.byref(mask))
+    scale = ctypes.c_float()
+    bias = ctypes.c_uint32()
+    n = lib.hlwq_search_table(kind, None, 0, None, ctypes.byref(scale), ctypes.byref(bias))
     if n < 0:
         _check("hlwq_search_table", n)
-    buf = (ctypes.c_uint32 * (4 * n))()
-    lib.hlwq_search_table(kind, buf, n, ctypes.byref(off), ctypes.byref(mask))
-    return np.frombuffer(buf, dtype=np.uint32).reshape(n, 4).copy(), float(off.value), int(mask.value)
+    K = 32 if kind == 0 else 8
+    buckets = (ctypes.c_uint8 * n)()
+    entries = (ctypes.c_uint32 * (2 * K))()
+    lib.hlwq_search_table(kind, buckets, n, entries, ctypes.byref(scale), ctypes.byref(bias))
+    return (np.frombuffer(buckets, dtype=np.uint8).copy(), np.frombuffer(entries, dtype=np.uint32).reshape(K, 2).copy(),
+            float(scale.value), int(bias.value))
 
 
 # --------------------------------------------------------------------------

@@ -8,32 +8,35 @@
 //   * the decision thresholds: the largest fp32 value not above the exact
 //     midpoint of two neighbouring fp32 centroids, so "number of thresholds
 //     strictly below y" is the index of the nearest centroid, ties low;
-//   * the bucket table the kernels use to find a code with one compare.
+//   * the two tables the kernels use to find a code with one compare.
 //
 // Bucket search.  For a rotated value y the kernels form, in fp32,
-//   u = y + O            (one rounding; O lies in [2^16, 2^17), ulp 1/128)
-// and read 8 bytes at LDS byte offset  bits(u) & MASK.  Every u the kernels
-// can produce lies in one aligned window of that binade in which mantissa
-// bits 4 and up count buckets of width 1/8 (16 ulps), so the masked bits are
-// the byte offset of a 16-byte entry with no shift; bit 3 of u (which half of
-// its bucket y fell in) picks one of two identical 8-byte copies inside the
-// entry, which spreads the reads of a wave over twice as many LDS banks.  The entry is
-// {threshold t_k or +inf, base_k} and the code is base_k + (y > t_k).
-// Buckets are narrower than the smallest gap between thresholds, so each holds
-// at most one threshold; base_k counts the thresholds below the bucket.  The
-// add is monotone and the bucket edges are representable, so rounding can only
-// move a y lying at most 1/256 below an edge up into the next bucket; the
-// result stays exact as long as no threshold lies that close below an edge.
-// The phase of the edges (O modulo 1/8) is chosen per table to keep every
-// threshold at least 1/128 below the next edge; this program then verifies the
-// search by brute force against the plain count on every fp32 value near
-// every threshold and edge, plus a dense sweep, and exits non-zero (failing
-// the build) on any disagreement.
+//   u = fma(y, 2^-146, bias)       bias = C * 2^-149, a denormal, C even
+// with one rounding.  For every reachable y the exact value 8 y 2^-149 + bias
+// lies in the denormal range, whose spacing is 2^-149, so the bit pattern of u
+// is the integer k = RN(8 y + C) (ties to even): the index of a bucket of
+// width 1/8.  k is used as a byte address with no masking:
+//   bucket table  B[k] = 8 * base_k, base_k = number of thresholds below every
+//                 y of bucket k;
+//   entry table   E[b] = {threshold b (+inf for b = K - 1), b}, 8 bytes each;
+//   code          = E[B[k]].b + (y > E[B[k]].threshold).
+// The thresholds are further apart than 1/8, so a bucket holds at most one
+// threshold, which is then threshold base_k; every other threshold is below
+// all of the bucket or not below any of it, and the compare settles the rest.
+// This program checks both facts and then verifies the search by brute force
+// against the plain count on every fp32 value near every threshold and bucket
+// edge, plus a dense sweep, and exits non-zero (failing the build) on any
+// disagreement.
 //
-// |y| <= sqrt(128) * (1 + 2e-6) for every finite 128-block (Cauchy-Schwarz on
-// the unit-norm rotated block), inside the 32-wide window of the weight
-// tables (256 entries, MASK 0xff8); 256-wide KV vectors reach |y| <= 16, so
-// their table spans a 64-wide window (512 entries, MASK 0x1ff8).
+// Reach.  Let S be the exact squared norm of a block and s the computed one.
+// Each of the R roundings of the norm sum (191 for a 128-block, 383 for a
+// 256-vector) errs by at most 2^-24 of its result or 2^-150, so with s >= 2^-149
+// (the smallest non-zero value) S / s <= (1 + 2^-24 R)(1 + R / 2).  As every
+// rotated value obeys |z| <= sqrt(L S), |y| = |z| / s^(1/2) stays below
+// sqrt(128 * 96.5) < 112 for weights and sqrt(256 * 192.5) < 222 for KV
+// vectors (including the fp32 error of the butterflies), inside the 2048- and
+// 4096-bucket tables (|y| < 128 and < 256).  Blocks whose squares underflow are
+// exactly where s underestimates S; for the rest |y| <= sqrt(L) (1 + 2e-6).
 
 #include <cinttypes>
 #include <cmath>
@@ -97,12 +100,20 @@ uint32_t f2u(float f) {
   return u;
 }
 
+float u2f(uint32_t u) {
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+constexpr float kScale = 0x1p-146f;  // 8 * 2^-149
+
 struct Tables {
   int K;
   std::vector<float> cent, thr;
-  std::vector<uint32_t> search;  // 16-byte entries {threshold bits, base} x 2
-  float offset = 0.0f;           // O
-  uint32_t mask = 0;             // byte-offset mask of bits(u)
+  std::vector<uint8_t> bucket;   // B[k] = 8 * base_k
+  std::vector<uint32_t> entry;   // E[b] = {threshold bits, b}
+  uint32_t bias = 0;             // bits of the denormal bias (= C)
 };
 
 // code by definition: number of thresholds strictly below y
@@ -112,28 +123,20 @@ uint32_t count_code(const std::vector<float>& thr, float y) {
   return n;
 }
 
-constexpr double kU0 = 98304.0;  // 1.5 * 2^16: start of the window, low 13 mantissa bits zero
-
+// the kernels' search, with the same single-rounding fused multiply-add
 uint32_t bucket_code(const Tables& tb, float y) {
-  const float u = y + tb.offset;  // one fp32 rounding, as on the device
-  uint32_t bits;
-  std::memcpy(&bits, &u, 4);
-  const uint32_t off = (bits & tb.mask) >> 2;  // word index of the 8-byte copy read
-  float t;
-  std::memcpy(&t, &tb.search[off], 4);
-  return tb.search[off + 1] + ((y > t) ? 1u : 0u);
+  const uint32_t k = f2u(std::fmaf(y, kScale, u2f(tb.bias)));
+  if (k >= tb.bucket.size()) {
+    std::fprintf(stderr, "gen_tables: bucket index %u out of range at y=%a\n", k, y);
+    std::exit(1);
+  }
+  const uint32_t e = tb.bucket[k] / 4u;
+  return tb.entry[e + 1] + ((y > u2f(tb.entry[e])) ? 1u : 0u);
 }
 
-// y-interval [lo, hi) of bucket k for window offset O
-void bucket_range(int k, double O, double* lo, double* hi) {
-  *lo = kU0 + k / 8.0 - O;
-  *hi = kU0 + (k + 1) / 8.0 - O;
-}
-
-Tables make_tables(int K, int entries, uint32_t mask) {
+Tables make_tables(int K, int buckets) {
   Tables tb;
   tb.K = K;
-  tb.mask = mask;
   const std::vector<double> c = lloyd_max(K);
   for (double v : c) tb.cent.push_back((float)v);
   for (int k = 0; k + 1 < K; ++k) {
@@ -142,59 +145,37 @@ Tables make_tables(int K, int entries, uint32_t mask) {
     if ((double)b > m) b = std::nextafterf(b, -INFINITY);
     tb.thr.push_back(b);
   }
-  // window centred on y = 0; the phase (steps of 1/64) is chosen to keep the
-  // largest distance between every threshold and the bucket edge above it
-  // (only a value just below an edge can be rounded into the next bucket)
-  const double half = entries / 16.0;  // half the window width in y
-  double best_phase = -1, best_gap = -1;
-  for (int j = 0; j < 16; ++j) {
-    const double phase = j / 128.0;
-    double gap = 1e9;
-    for (float t : tb.thr) {
-      const double r = std::fmod((double)t + half + phase, 0.125);  // position inside its bucket
-      const double rr = r < 0 ? r + 0.125 : r;
-      gap = std::fmin(gap, 0.125 - rr);
+  for (int k = 0; k + 2 < K; ++k) {
+    if (!((double)tb.thr[k + 1] - (double)tb.thr[k] > 0.125)) {
+      std::fprintf(stderr, "gen_tables: thresholds closer than one bucket (K=%d)\n", K);
+      std::exit(1);
     }
-    if (gap > best_gap) { best_gap = gap; best_phase = phase; }
   }
-  if (best_gap < 1.0 / 128.0) {
-    std::fprintf(stderr, "gen_tables: no bucket phase keeps thresholds 1/128 below the edges (K=%d)\n", K);
-    std::exit(1);
-  }
-  const double O = kU0 + half + best_phase;
-  tb.offset = (float)O;
-  if ((double)tb.offset != O) {
-    std::fprintf(stderr, "gen_tables: window offset not representable\n");
-    std::exit(1);
-  }
-  for (int k = 0; k < entries; ++k) {
-    double lo, hi;
-    bucket_range(k, O, &lo, &hi);
-    uint32_t base = 0;
-    int inside = 0;
-    float t_in = INFINITY;
+  const int C = buckets / 2;  // even; bucket C holds y = 0
+  tb.bias = (uint32_t)C;
+  // bucket k holds the y with k - 1/2 <= 8 y + C <= k + 1/2 (ties to even)
+  for (int k = 0; k < buckets; ++k) {
+    const double lo = (k - C - 0.5) / 8.0, hi = (k - C + 0.5) / 8.0;
+    int base = 0, inside = 0;
     for (float t : tb.thr) {
       if ((double)t < lo) ++base;
-      else if ((double)t < hi) { ++inside; t_in = t; }
+      else if ((double)t < hi) ++inside;
     }
     if (inside > 1) {
       std::fprintf(stderr, "gen_tables: bucket %d holds %d thresholds\n", k, inside);
       std::exit(1);
     }
-    tb.search.push_back(f2u(t_in));
-    tb.search.push_back(base);
-    tb.search.push_back(f2u(t_in));
-    tb.search.push_back(base);
+    tb.bucket.push_back((uint8_t)(8 * base));
   }
-  // brute-force verification over the reachable range |y| < half - 1/8
-  const float ymax = (float)(half - 0.25);
+  for (int b = 0; b < K; ++b) {
+    tb.entry.push_back(b + 1 < K ? f2u(tb.thr[b]) : f2u(INFINITY));
+    tb.entry.push_back((uint32_t)b);
+  }
+  // brute-force verification over the reachable range |y| < buckets / 16
+  const float ymax = (float)(buckets / 16.0 - 0.125);
   std::vector<float> probes;
   for (float t : tb.thr) probes.push_back(t);
-  for (int k = 0; k <= entries; ++k) {
-    double lo, hi;
-    bucket_range(k, O, &lo, &hi);
-    probes.push_back((float)lo);
-  }
+  for (int k = 0; k <= buckets; ++k) probes.push_back((float)((k - C - 0.5) / 8.0));
   probes.push_back(0.0f);
   for (float p : probes) {
     float lo = p, hi = p;
@@ -217,9 +198,9 @@ Tables make_tables(int K, int entries, uint32_t mask) {
       std::exit(1);
     }
   }
-  for (float y : {0.0f, -0.0f}) {
+  for (float y : {0.0f, -0.0f, 0x1p-149f, -0x1p-149f, 0x1p-126f, -0x1p-126f}) {
     if (count_code(tb.thr, y) != bucket_code(tb, y)) {
-      std::fprintf(stderr, "gen_tables: bucket search wrong at signed zero\n");
+      std::fprintf(stderr, "gen_tables: bucket search wrong at y=%a\n", y);
       std::exit(1);
     }
   }
@@ -234,30 +215,42 @@ void emit_floats(const char* name, const std::vector<float>& v) {
 
 void emit_words(const char* name, const std::vector<uint32_t>& v) {
   std::printf("#define %s { \\\n", name);
-  for (size_t i = 0; i < v.size(); i += 4)
-    std::printf("  0x%08" PRIx32 "u, %" PRIu32 "u, 0x%08" PRIx32 "u, %" PRIu32 "u%s\n", v[i], v[i + 1], v[i + 2],
-                v[i + 3], i + 4 < v.size() ? ", \\" : " }");
+  for (size_t i = 0; i < v.size(); i += 2)
+    std::printf("  0x%08" PRIx32 "u, %" PRIu32 "u%s\n", v[i], v[i + 1], i + 2 < v.size() ? ", \\" : " }");
+}
+
+// bucket bytes packed little-endian into 32-bit words (the kernels copy words)
+void emit_bytes(const char* name, const std::vector<uint8_t>& v) {
+  std::printf("#define %s { \\\n", name);
+  for (size_t i = 0; i < v.size(); i += 16) {
+    std::printf(" ");
+    for (size_t j = i; j < i + 16; j += 4) {
+      const uint32_t w = v[j] | (v[j + 1] << 8) | (v[j + 2] << 16) | ((uint32_t)v[j + 3] << 24);
+      std::printf(" 0x%08" PRIx32 "u%s", w, j + 4 < v.size() ? "," : "");
+    }
+    std::printf("%s\n", i + 16 < v.size() ? " \\" : " }");
+  }
 }
 
 }  // namespace
 
 int main() {
-  const Tables q5 = make_tables(32, 256, 0xff8u);
-  const Tables q3 = make_tables(8, 256, 0xff8u);
-  const Tables kv3 = make_tables(8, 512, 0x1ff8u);
+  const Tables q5 = make_tables(32, 2048);
+  const Tables q3 = make_tables(8, 2048);
+  const Tables kv3 = make_tables(8, 4096);
   std::printf("// Generated at build time by gen_tables.cpp: Lloyd-Max tables for N(0,1).\n");
   std::printf("#pragma once\n");
-  std::printf("#define HLWQ_SEARCH_ENTRIES 256\n#define HLWQ_SEARCH_MASK 0xff8u\n");
-  std::printf("#define HLWQ_SEARCH_OFFSET_5 %af\n#define HLWQ_SEARCH_OFFSET_3 %af\n", (double)q5.offset,
-              (double)q3.offset);
-  std::printf("#define HLWQ_KV_SEARCH_ENTRIES 512\n#define HLWQ_KV_SEARCH_MASK 0x1ff8u\n");
-  std::printf("#define HLWQ_KV_SEARCH_OFFSET %af\n", (double)kv3.offset);
+  std::printf("#define HLWQ_SEARCH_SCALE %af\n", (double)kScale);
+  std::printf("#define HLWQ_BUCKETS %zu\n#define HLWQ_BUCKET_BIAS %uu\n", q5.bucket.size(), q5.bias);
+  std::printf("#define HLWQ_KV_BUCKETS %zu\n#define HLWQ_KV_BUCKET_BIAS %uu\n", kv3.bucket.size(), kv3.bias);
   emit_floats("HLWQ_CENTROIDS_5", q5.cent);
   emit_floats("HLWQ_THRESHOLDS_5", q5.thr);
-  emit_words("HLWQ_SEARCH_5", q5.search);
+  emit_bytes("HLWQ_BUCKET_5", q5.bucket);
+  emit_words("HLWQ_ENTRY_5", q5.entry);
   emit_floats("HLWQ_CENTROIDS_3", q3.cent);
   emit_floats("HLWQ_THRESHOLDS_3", q3.thr);
-  emit_words("HLWQ_SEARCH_3", q3.search);
-  emit_words("HLWQ_KV_SEARCH_3", kv3.search);
+  emit_bytes("HLWQ_BUCKET_3", q3.bucket);
+  emit_words("HLWQ_ENTRY_3", q3.entry);
+  emit_bytes("HLWQ_KV_BUCKET_3", kv3.bucket);
   return 0;
 }

@@ -13,14 +13,14 @@
 // only the last norm level and the last butterfly stage (stride 128) cross
 // lanes, through a DPP quad permutation.
 //
-// Code search.  A rotated value y picks the entry {threshold, base} of a small
-// LDS table at byte offset bits(y + O) & mask (O puts every reachable y + O in
-// one binade whose low mantissa bits count 1/8-wide buckets); the code is
-// base + (y > threshold).
-// The table is built and proven exact against the plain count at build time
-// (gen_tables.cpp), so the kernels reproduce "number of fp32 thresholds below
-// y" bit for bit with one compare.
-//
+// Code search.  A rotated value y becomes, by one fused multiply-add with a
+// denormal addend, a denormal whose bit pattern is the index of its 1/8-wide
+// bucket; one LDS byte read there gives the offset of the entry
+// {threshold, base} in a second small table, and the code is
+// base + (y > threshold).  The tables are built and proven exact against the
+// plain count at build time (gen_tables.cpp), so the kernels reproduce
+// "number of fp32 thresholds below y" bit for bit with one compare.
+
 // Rounding.  The file is compiled with -ffp-contract=off: every + and * below
 // is one IEEE round-to-nearest operation in the order written, sqrtf and the
 // division are correctly rounded, and the only fused multiply-adds are the
@@ -48,17 +48,21 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __constant__ float c_cent5[32] = HLWQ_CENTROIDS_5;
 __constant__ float c_cent3[8] = HLWQ_CENTROIDS_3;
-__constant__ uint32_t c_search5[4 * HLWQ_SEARCH_ENTRIES] = HLWQ_SEARCH_5;
-__constant__ uint32_t c_search3[4 * HLWQ_SEARCH_ENTRIES] = HLWQ_SEARCH_3;
-__constant__ uint32_t c_kvsearch3[4 * HLWQ_KV_SEARCH_ENTRIES] = HLWQ_KV_SEARCH_3;
+__constant__ uint32_t c_bucket5[HLWQ_BUCKETS / 4] = HLWQ_BUCKET_5;
+__constant__ uint32_t c_bucket3[HLWQ_BUCKETS / 4] = HLWQ_BUCKET_3;
+__constant__ uint32_t c_kvbucket3[HLWQ_KV_BUCKETS / 4] = HLWQ_KV_BUCKET_3;
+__constant__ uint32_t c_entry5[2 * 32] = HLWQ_ENTRY_5;
+__constant__ uint32_t c_entry3[2 * 8] = HLWQ_ENTRY_3;
 
 const float h_cent5[32] = HLWQ_CENTROIDS_5;
 const float h_thr5[31] = HLWQ_THRESHOLDS_5;
 const float h_cent3[8] = HLWQ_CENTROIDS_3;
 const float h_thr3[7] = HLWQ_THRESHOLDS_3;
-const uint32_t h_search5[4 * HLWQ_SEARCH_ENTRIES] = HLWQ_SEARCH_5;
-const uint32_t h_search3[4 * HLWQ_SEARCH_ENTRIES] = HLWQ_SEARCH_3;
-const uint32_t h_kvsearch3[4 * HLWQ_KV_SEARCH_ENTRIES] = HLWQ_KV_SEARCH_3;
+const uint32_t h_bucket5[HLWQ_BUCKETS / 4] = HLWQ_BUCKET_5;
+const uint32_t h_bucket3[HLWQ_BUCKETS / 4] = HLWQ_BUCKET_3;
+const uint32_t h_kvbucket3[HLWQ_KV_BUCKETS / 4] = HLWQ_KV_BUCKET_3;
+const uint32_t h_entry5[2 * 32] = HLWQ_ENTRY_5;
+const uint32_t h_entry3[2 * 8] = HLWQ_ENTRY_3;
 
 // ---------------------------------------------------------------------------
 // device helpers
@@ -198,16 +202,20 @@ __device__ __forceinline__ NormInfo norm_info(float s) {
   return ni;
 }
 
-// Code of one rotated value: y = z * r, then one read of the bucket table
-// (16-byte entries {threshold, base, -, -}) at byte offset bits(y + offset) &
-// mask, and one compare.  The table generator proves this equals the number
-// of fp32 thresholds strictly below y for every reachable y.
-__device__ __forceinline__ uint32_t code_of(float z, float r, const uint8_t* __restrict__ tab, float offset,
-                                            uint32_t mask) {
+// Code of one rotated value y = z * r.  u = fma(y, 2^-146, bias) is a
+// denormal for every reachable y (bias = C * 2^-149), so bits(u) = RN(8 y) + C
+// is the index of y's 1/8-wide bucket; the byte there (bucket table at LDS
+// byte offset `bucket`) is the offset of the entry {threshold, base} in the
+// entry table at LDS offset 0, and the code is base + (y > threshold).  The
+// table generator proves this equals the number of fp32 thresholds strictly
+// below y for every reachable y.
+__device__ __forceinline__ uint32_t code_of(float z, float r, const uint8_t* __restrict__ lds, uint32_t bucket,
+                                            float bias) {
   const float y = z * r;
-  const uint32_t off = __float_as_uint(y + offset) & mask;
-  const uint2 e = *reinterpret_cast<const uint2*>(tab + off);
-  return e.y + ((y > __uint_as_float(e.x)) ? 1u : 0u);
+  const uint32_t k = __float_as_uint(__builtin_fmaf(y, HLWQ_SEARCH_SCALE, bias));
+  const uint32_t e = lds[bucket + k];
+  const uint2 v = *reinterpret_cast<const uint2*>(lds + e);
+  return v.y + ((y > __uint_as_float(v.x)) ? 1u : 0u);
 }
 
 // Encode L values into L * BITS / 32 words: 8 codes of BITS bits per group,
@@ -216,8 +224,8 @@ __device__ __forceinline__ uint32_t code_of(float z, float r, const uint8_t* __r
 // code; a code that straddles two words is computed once, finishes the upper
 // word's bottom bits and starts the lower word.
 template <int BITS, int L>
-__device__ __forceinline__ void encode(const float (&z)[L], float r, const uint8_t* __restrict__ tab, float offset,
-                                       uint32_t mask, uint32_t (&w)[L * BITS / 32]) {
+__device__ __forceinline__ void encode(const float (&z)[L], float r, const uint8_t* __restrict__ lds, uint32_t bucket,
+                                       float bias, uint32_t (&w)[L * BITS / 32]) {
   constexpr int W = L * BITS / 32;
   uint32_t carry = 0;  // straddling code shared with the word below
 #pragma unroll
@@ -226,11 +234,11 @@ __device__ __forceinline__ void encode(const float (&z)[L], float r, const uint8
     const int jlo = (32 * wi + BITS - 1) / BITS;        // first code starting in this word
     const int off = BITS * jlo - 32 * wi;               // its bit position (0 .. BITS-1)
     const bool top_shared = (BITS * jhi + BITS > 32 * (wi + 1)) && (jhi < L);
-    uint32_t acc = top_shared ? carry : code_of(z[jhi], r, tab, offset, mask);
+    uint32_t acc = top_shared ? carry : code_of(z[jhi], r, lds, bucket, bias);
 #pragma unroll
-    for (int j = jhi - 1; j >= jlo; --j) acc = (acc << BITS) + code_of(z[j], r, tab, offset, mask);
+    for (int j = jhi - 1; j >= jlo; --j) acc = (acc << BITS) + code_of(z[j], r, lds, bucket, bias);
     if (off > 0) {
-      const uint32_t c = code_of(z[jlo - 1], r, tab, offset, mask);
+      const uint32_t c = code_of(z[jlo - 1], r, lds, bucket, bias);
       acc = (acc << off) + (c >> (BITS - off));
       carry = c;
     }
@@ -451,14 +459,16 @@ __device__ __forceinline__ BatchPos batch_pos(const WeightGroup& g, int d, uint3
 
 template <int BITS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_quantize_kernel(const WeightGroup g) {
-  // one LDS array: the bucket table at offset 0 (so table reads need no base
-  // add), then the 256-byte aligned per-wave stages
-  constexpr int kTab = 16 * HLWQ_SEARCH_ENTRIES;
+  // one LDS array: the entry table at offset 0 (so its reads need no base
+  // add), the bucket table, then the 256-byte aligned per-wave stages
+  constexpr int kTab = 256 + HLWQ_BUCKETS;
   __shared__ __attribute__((aligned(256))) uint8_t lds[kTab + kWaves * kStage];
   uint32_t* tab = reinterpret_cast<uint32_t*>(lds);
   uint8_t* stage_all = lds + kTab;
-  const uint32_t* src_tab = (BITS == 5) ? c_search5 : c_search3;
-  for (int i = threadIdx.x; i < 4 * HLWQ_SEARCH_ENTRIES; i += kThreads) tab[i] = src_tab[i];
+  const uint32_t* src_bucket = (BITS == 5) ? c_bucket5 : c_bucket3;
+  const uint32_t* src_entry = (BITS == 5) ? c_entry5 : c_entry3;
+  for (int i = threadIdx.x; i < HLWQ_BUCKETS / 4; i += kThreads) tab[64 + i] = src_bucket[i];
+  if (threadIdx.x < 2 * (1 << BITS)) tab[threadIdx.x] = src_entry[threadIdx.x];
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -492,8 +502,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     const NormInfo ni = norm_info(sumsq_tree(x));
     fwht(x);
     uint32_t words[4 * BITS];
-    encode<BITS, kBlock>(x, ni.r, reinterpret_cast<const uint8_t*>(tab),
-                         (BITS == 5) ? HLWQ_SEARCH_OFFSET_5 : HLWQ_SEARCH_OFFSET_3, HLWQ_SEARCH_MASK, words);
+    encode<BITS, kBlock>(x, ni.r, lds, 256u, __uint_as_float(HLWQ_BUCKET_BIAS), words);
 
     // packed output of the batch is contiguous: kOut bytes per block
 #pragma unroll
@@ -599,11 +608,13 @@ __device__ __forceinline__ KvPos kv_pos(const KvArgs& a, uint32_t b, int lane) {
 }
 
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_kv_quantize_kernel(const KvArgs a) {
-  constexpr int kTab = 16 * HLWQ_KV_SEARCH_ENTRIES;
+  // entry table at offset 0, bucket table, per-wave stages
+  constexpr int kTab = 256 + HLWQ_KV_BUCKETS;
   __shared__ __attribute__((aligned(256))) uint8_t lds[kTab + kWaves * kStage];
   uint32_t* tab = reinterpret_cast<uint32_t*>(lds);
   uint8_t* stage_all = lds + kTab;
-  for (int i = threadIdx.x; i < 4 * HLWQ_KV_SEARCH_ENTRIES; i += kThreads) tab[i] = c_kvsearch3[i];
+  for (int i = threadIdx.x; i < HLWQ_KV_BUCKETS / 4; i += kThreads) tab[64 + i] = c_kvbucket3[i];
+  if (threadIdx.x < 16) tab[threadIdx.x] = c_entry3[threadIdx.x];
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -637,8 +648,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     for (int j = 0; j < kBlock; ++j) x[j] = cross_pair(x[j], sgn);
 
     uint32_t words[12];
-    encode<3, kBlock>(x, ni.r, reinterpret_cast<const uint8_t*>(tab), HLWQ_KV_SEARCH_OFFSET, HLWQ_KV_SEARCH_MASK,
-                      words);
+    encode<3, kBlock>(x, ni.r, lds, 256u, __uint_as_float(HLWQ_KV_BUCKET_BIAS), words);
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
       const u32x4 v = {words[4 * q], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]};
@@ -922,26 +932,26 @@ int hlwq_centroids(int bits, float* centroids, float* thresholds) {
   return HLWQ_OK;
 }
 
-int hlwq_search_table(int kind, uint32_t* words, int capacity, float* offset, uint32_t* mask) {
-  const uint32_t* src;
-  int entries;
-  float off;
-  uint32_t m;
+int hlwq_search_table(int kind, uint8_t* buckets, int capacity, uint32_t* entries, float* scale,
+                      uint32_t* bias_bits) {
+  const uint32_t* bucket;
+  const uint32_t* entry;
+  int n, K;
+  uint32_t bias;
   switch (kind) {
-    case 0: src = h_search5; entries = HLWQ_SEARCH_ENTRIES; off = HLWQ_SEARCH_OFFSET_5; m = HLWQ_SEARCH_MASK; break;
-    case 1: src = h_search3; entries = HLWQ_SEARCH_ENTRIES; off = HLWQ_SEARCH_OFFSET_3; m = HLWQ_SEARCH_MASK; break;
-    case 2:
-      src = h_kvsearch3; entries = HLWQ_KV_SEARCH_ENTRIES; off = HLWQ_KV_SEARCH_OFFSET; m = HLWQ_KV_SEARCH_MASK;
-      break;
+    case 0: bucket = h_bucket5; entry = h_entry5; n = HLWQ_BUCKETS; K = 32; bias = HLWQ_BUCKET_BIAS; break;
+    case 1: bucket = h_bucket3; entry = h_entry3; n = HLWQ_BUCKETS; K = 8; bias = HLWQ_BUCKET_BIAS; break;
+    case 2: bucket = h_kvbucket3; entry = h_entry3; n = HLWQ_KV_BUCKETS; K = 8; bias = HLWQ_KV_BUCKET_BIAS; break;
     default: return HLWQ_ERR_BITS;
   }
-  if (words) {
-    const int n = capacity < entries ? capacity : entries;
-    if (n > 0) std::memcpy(words, src, sizeof(uint32_t) * 4 * n);
+  if (buckets) {
+    const int m = capacity < n ? capacity : n;
+    if (m > 0) std::memcpy(buckets, bucket, static_cast<size_t>(m));
   }
-  if (offset) *offset = off;
-  if (mask) *mask = m;
-  return entries;
+  if (entries) std::memcpy(entries, entry, sizeof(uint32_t) * 2 * K);
+  if (scale) *scale = HLWQ_SEARCH_SCALE;
+  if (bias_bits) *bias_bits = bias;
+  return n;
 }
 
 const char* hlwq_status_string(int status) {
