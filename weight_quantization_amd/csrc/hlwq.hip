@@ -175,11 +175,12 @@ __device__ __forceinline__ float sumsq_tree(const float (&x)[L]) {
   return s[0];
 }
 
-// Unnormalised Walsh-Hadamard butterflies, strides 1, 2, ..., L/2 (natural order).
-template <int L>
+// Unnormalised Walsh-Hadamard butterflies, strides H0, 2 H0, ..., L/2 (natural
+// order; H0 = 1 is the whole transform).
+template <int L, int H0 = 1>
 __device__ __forceinline__ void fwht(float (&v)[L]) {
 #pragma unroll
-  for (int h = 1; h < L; h <<= 1)
+  for (int h = H0; h < L; h <<= 1)
 #pragma unroll
     for (int i = 0; i < L; ++i)
       if ((i & h) == 0) {
@@ -246,16 +247,41 @@ __device__ __forceinline__ void encode(const float (&z)[L], float r, const uint8
   }
 }
 
-// Unpack L codes of BITS bits and look up their centroids.
+// Unpack L codes of BITS bits, look up their centroids and apply the first
+// butterfly stage, two values at a time.  Stage 1 pairs exactly the two codes
+// of a pair index (codes are LSB-first, so code 2m is the low half of pair m),
+// so the pair table (LDS offset 0) holds, for every 2*BITS-bit index i with
+// a = i mod 2^BITS and b = i >> BITS, the stage-1 outputs
+// {c[a] + c[b], c[a] - c[b]}, computed with the same fp32 operations.  One
+// 8-byte read serves two values; its byte offset 8 i comes out of the packed
+// words with one shift or funnel shift and one mask.
 template <int BITS, int L>
-__device__ __forceinline__ void decode(const uint32_t (&w)[L * BITS / 32], const float* __restrict__ cent,
-                                       float (&v)[L]) {
+__device__ __forceinline__ void decode_stage1(const uint32_t (&w)[L * BITS / 32], const uint8_t* __restrict__ pairs,
+                                              float (&v)[L]) {
+  constexpr uint32_t kMask = ((1u << (2 * BITS)) - 1u) << 3;
 #pragma unroll
-  for (int j = 0; j < L; ++j) {
-    const int p = j * BITS;
-    uint32_t code = w[p >> 5] >> (p & 31);
-    if ((p & 31) + BITS > 32) code |= w[(p >> 5) + 1] << (32 - (p & 31));
-    v[j] = cent[code & ((1u << BITS) - 1u)];
+  for (int m = 0; m < L / 2; ++m) {
+    const int p = 2 * BITS * m;  // bit position of pair m
+    const int lo = p & 31, wi = p >> 5;
+    uint32_t off;
+    if (lo + 2 * BITS <= 32)
+      off = (lo >= 3) ? (w[wi] >> (lo - 3)) : (w[wi] << (3 - lo));
+    else
+      off = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], lo - 3);
+    const float2 c = *reinterpret_cast<const float2*>(pairs + (off & kMask));
+    v[2 * m] = c.x;
+    v[2 * m + 1] = c.y;
+  }
+}
+
+// Fill the pair table of a K-centroid codebook (K * K entries of 8 bytes).
+template <int BITS>
+__device__ __forceinline__ void fill_pairs(float* pairs, const float* __restrict__ cent) {
+  constexpr int K = 1 << BITS;
+  for (int i = threadIdx.x; i < K * K; i += kThreads) {
+    const float a = cent[i & (K - 1)], b = cent[i >> BITS];
+    pairs[2 * i] = a + b;
+    pairs[2 * i + 1] = a - b;
   }
 }
 
@@ -280,9 +306,19 @@ constexpr int kStage = 16384;          // LDS bytes per wave
 
 __device__ __forceinline__ uint32_t swz(uint32_t q) { return q ^ ((q >> 4) & 15u); }
 
+// streaming (nontemporal) accesses: cache-policy bit 1
+constexpr int kNt = 2;
+
 // wait for this wave's outstanding vector-memory operations, including the
 // direct-to-LDS loads; the memory clobber keeps LDS reads below it
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Lanes of a wave hand data to each other through LDS (one lane writes a
+// slot, another reads it).  A wave's LDS operations execute in order, but the
+// compiler reasons per lane and may, for instance, keep a value a lane loaded
+// before another lane's write; this compiler barrier marks each hand-over, so
+// no access moves across it and nothing loaded before it is reused after it.
+__device__ __forceinline__ void lds_handover() { asm volatile("" ::: "memory"); }
 
 // Per-lane byte offsets of the swizzled slot pattern: in load / store
 // instruction i, lane l handles chunk 64 i + (l ^ (4 (i & 3) + (l >> 4))),
@@ -308,14 +344,15 @@ __device__ __forceinline__ SwzLane swz_lane(int lane) {
 
 // Stage `bytes` (<= 1024 * NI) of global memory starting at the 16-byte
 // aligned address src: chunk q (16 bytes) lands in slot swz(q) if SWZ, else q.
-// Chunks past `bytes` re-read src and are never consumed.
-template <int NI, bool SWZ>
+// Chunks past `bytes` re-read src and are never consumed.  AUX is the cache
+// policy of the loads.
+template <int NI, bool SWZ, int AUX>
 __device__ __forceinline__ void stage_in(const uint8_t* src, uint32_t bytes, uint8_t* stage, int lane,
                                          const SwzLane& sl) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const uint32_t off = 1024u * i + (SWZ ? sl.o[i & 3] : 16u * lane);
-    __builtin_amdgcn_global_load_lds(src + (off < bytes ? off : 0u), stage + 1024 * i, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src + (off < bytes ? off : 0u), stage + 1024 * i, 16, 0, AUX);
   }
 }
 
@@ -324,6 +361,7 @@ __device__ __forceinline__ void stage_in(const uint8_t* src, uint32_t bytes, uin
 template <int NI, bool SWZ>
 __device__ __forceinline__ void stage_out(uint8_t* dst, uint32_t bytes, const uint8_t* stage, int lane,
                                           const SwzLane& sl) {
+  lds_handover();
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const uint32_t q = 64u * i + lane;
@@ -332,6 +370,7 @@ __device__ __forceinline__ void stage_out(uint8_t* dst, uint32_t bytes, const ui
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + 16u * q));
     }
   }
+  lds_handover();
 }
 
 __device__ __forceinline__ int64_t first_lane64(int64_t v) {
@@ -379,9 +418,20 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 __device__ __forceinline__ u32x4 lds_read16(uint32_t a) { return *(const lds_u32x4*)a; }
 __device__ __forceinline__ void lds_write16(uint32_t a, u32x4 v) { *(lds_u32x4*)a = v; }
 
-__device__ __forceinline__ void stage_in_full(const uint8_t* src, uint8_t* stage, const SwzLane& sl) {
+// Buffer resource over `bytes` bytes at `base` (raw, unswizzled): the full
+// paths address a batch as base + per-lane VGPR offset + scalar offset, so
+// their loads and stores need no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t batch_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// Stage a full batch (16 KB, read once: streaming loads).
+__device__ __forceinline__ void stage_in_full(__amdgpu_buffer_rsrc_t src, uint8_t* stage, const SwzLane& sl) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) __builtin_amdgcn_global_load_lds(src + 1024 * i + sl.o[i & 3], stage + 1024 * i, 16, 0, 0);
+  for (int i = 0; i < 16; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)(stage + 1024 * i), 16,
+                                             sl.o[i & 3], 1024 * i, 0, kNt);
 }
 
 __device__ __forceinline__ void read_block_full(uint32_t a, float (&x)[kBlock]) {
@@ -397,12 +447,15 @@ __device__ __forceinline__ void write_block_full(uint32_t a, const uint32_t (&pk
   }
 }
 
-__device__ __forceinline__ void stage_out_full(uint8_t* dst, uint32_t stage, const SwzLane& sl, int lane) {
+
+__device__ __forceinline__ void stage_out_full(__amdgpu_buffer_rsrc_t dst, uint32_t stage, const SwzLane& sl, int lane) {
+  lds_handover();
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const u32x4 v = lds_read16(stage + 1024u * i + sl.o[i & 3]);
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + 1024 * i + 16 * lane));
+    __builtin_amdgcn_raw_buffer_store_b128(v, dst, 16u * lane, 1024 * i, kNt);
   }
+  lds_handover();
 }
 
 // ---------------------------------------------------------------------------
@@ -485,14 +538,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 
     float x[kBlock];
     if (g.whole[d] && p.nvalid == 64u) {
-      stage_in_full(reinterpret_cast<const uint8_t*>(g.w[d] + static_cast<int64_t>(p.g0) * kBlock), stage, sl);
+      stage_in_full(batch_rsrc(g.w[d] + static_cast<int64_t>(p.g0) * kBlock, 64u * 2u * kBlock), stage, sl);
       wait_vmem();
       read_block_full(lane_a, x);
     } else if (g.staged[d]) {
       const int64_t e0 = first_lane64(p.e);
       const uint32_t off = static_cast<uint32_t>(p.e - e0) * 2u;
       const uint32_t end = __builtin_amdgcn_readlane(off + 2u * p.n, p.nvalid - 1);
-      stage_in<16, true>(reinterpret_cast<const uint8_t*>(g.w[d] + e0), end, stage, lane, sl);
+      stage_in<16, true, kNt>(reinterpret_cast<const uint8_t*>(g.w[d] + e0), end, stage, lane, sl);
       wait_vmem();
       read_staged_block(stage, off, p.n, x);
     } else {
@@ -517,12 +570,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 
 template <int BITS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_dequantize_kernel(const WeightGroup g) {
-  // one LDS array: the centroids at offset 0, then the per-wave stages
-  __shared__ __attribute__((aligned(256))) uint8_t lds[256 + kWaves * kStage];
-  float* cent = reinterpret_cast<float*>(lds);
-  uint8_t* stage_all = lds + 256;
-  const float* src_cent = (BITS == 5) ? c_cent5 : c_cent3;
-  if (threadIdx.x < (1 << BITS)) cent[threadIdx.x] = src_cent[threadIdx.x];
+  // one LDS array: the centroid pair table at offset 0, then the per-wave stages
+  constexpr int kPairs = 8 << (2 * BITS);
+  __shared__ __attribute__((aligned(256))) uint8_t lds[kPairs + kWaves * kStage];
+  uint8_t* stage_all = lds + kPairs;
+  fill_pairs<BITS>(reinterpret_cast<float*>(lds), (BITS == 5) ? c_cent5 : c_cent3);
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -537,7 +589,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     const int d = group_of(g, b);
     const BatchPos p = batch_pos(g, d, b, lane);
 
-    stage_in<BITS, false>(g.packed[d] + static_cast<size_t>(p.g0) * kIn, p.nvalid * kIn, stage, lane, sl);
+    stage_in<BITS, false, 0>(g.packed[d] + static_cast<size_t>(p.g0) * kIn, p.nvalid * kIn, stage, lane, sl);
     const float scale = f16_value(g.norms[d][p.lb]) * 0x1p-7f;
     wait_vmem();
     // lanes past the end of the batch read (and later write) the last block
@@ -553,15 +605,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     }
 
     float v[kBlock];
-    decode<BITS, kBlock>(words, cent, v);
-    fwht(v);
+    decode_stage1<BITS, kBlock>(words, lds, v);
+    fwht<kBlock, 2>(v);
     uint32_t pk[kBlock / 2];
 #pragma unroll
     for (int j = 0; j < kBlock; j += 2) pk[j / 2] = pack_bf16x2(v[j] * scale, v[j + 1] * scale);
 
     if (g.whole[d] && p.nvalid == 64u) {
       write_block_full(lane_a, pk);
-      stage_out_full(reinterpret_cast<uint8_t*>(g.w[d] + static_cast<int64_t>(p.g0) * kBlock), lds_addr(stage), sl,
+      stage_out_full(batch_rsrc(g.w[d] + static_cast<int64_t>(p.g0) * kBlock, 64u * 2u * kBlock), lds_addr(stage), sl,
                      lane);
     } else if (g.staged[d]) {
       const int64_t e0 = first_lane64(p.e);
@@ -629,11 +681,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv + (static_cast<int64_t>(p.bh) * a.tokens + p.t0) * kKvDim);
     float x[kBlock];
     if (p.nvalid == 32u) {  // 32 whole vectors: lane l's half-vector is at bytes [256 l, 256 l + 256)
-      stage_in_full(src, stage, sl);
+      stage_in_full(batch_rsrc(src, 64u * 2u * kBlock), stage, sl);
       wait_vmem();
       read_block_full(lane_a, x);
     } else {
-      stage_in<16, true>(src, p.nvalid * 2u * kKvDim, stage, lane, sl);
+      stage_in<16, true, kNt>(src, p.nvalid * 2u * kKvDim, stage, lane, sl);
       wait_vmem();
       read_staged_block(stage, (p.t - p.t0) * 2u * kKvDim + p.half * 2u * kBlock, kBlock, x);
     }
@@ -661,10 +713,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 }
 
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_kv_dequantize_kernel(const KvArgs a) {
-  __shared__ __attribute__((aligned(256))) uint8_t lds[256 + kWaves * kStage];
-  float* cent = reinterpret_cast<float*>(lds);
-  uint8_t* stage_all = lds + 256;
-  if (threadIdx.x < 8) cent[threadIdx.x] = c_cent3[threadIdx.x];
+  // centroid pair table at offset 0, then the per-wave stages
+  __shared__ __attribute__((aligned(256))) uint8_t lds[512 + kWaves * kStage];
+  uint8_t* stage_all = lds + 512;
+  fill_pairs<3>(reinterpret_cast<float*>(lds), c_cent3);
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -677,7 +729,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     refresh(sl, lane_a);
     const KvPos p = kv_pos(a, b, lane);
     const size_t vec0 = static_cast<size_t>(p.bh) * a.tq + p.t0;
-    stage_in<3, false>(a.packed + vec0 * 96, p.nvalid * 96u, stage, lane, sl);
+    stage_in<3, false, 0>(a.packed + vec0 * 96, p.nvalid * 96u, stage, lane, sl);
     const float scale = f16_value(a.norms[vec0 + (p.t - p.t0)]) * 0x1p-8f;
     wait_vmem();
     // lanes past the end of the batch read (and later write) the last vector
@@ -693,8 +745,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     }
 
     float v[kBlock];
-    decode<3, kBlock>(words, cent, v);
-    fwht(v);
+    decode_stage1<3, kBlock>(words, lds, v);
+    fwht<kBlock, 2>(v);
     // stride-128 stage across the lane pair, then scale and round to bf16
     const float sgn = pair_sign(p.half);
     uint32_t pk[kBlock / 2];
@@ -708,7 +760,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     uint8_t* dst = reinterpret_cast<uint8_t*>(a.kv + (static_cast<int64_t>(p.bh) * a.tokens + p.t0) * kKvDim);
     if (p.nvalid == 32u) {
       write_block_full(lane_a, pk);
-      stage_out_full(dst, lds_addr(stage), sl, lane);
+      stage_out_full(batch_rsrc(dst, 64u * 2u * kBlock), lds_addr(stage), sl, lane);
     } else {
       write_staged_block(stage, (p.t - p.t0) * 2u * kKvDim + p.half * 2u * kBlock, kBlock, pk);
       stage_out<16, true>(dst, p.nvalid * 2u * kKvDim, stage, lane, sl);
