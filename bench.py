@@ -144,28 +144,27 @@ def weight_workload(torch, wq, dev, config, bits):
 
 
 def kv_workload(torch, wq, dev, copies=2, n_residual=128):
+    """K and V of the cache held as one tensor [2 * batch, heads, tokens, 256]
+    (K first), so one launch encodes (or decodes) both."""
     sets = []
     for c in range(copies):
-        one = []
-        for t in ("K", "V"):
-            host = synth.kv_cache("kv_h256", t, seed=synth.DEFAULT_SEED + c)
-            kv = to_device(torch, dev, host)
-            p, n = wq.hlwq_kv_quantize(kv, n_residual=n_residual)
-            out = kv.clone()
-            one.append((kv, p, n, out))
-        sets.append(one)
+        host = np.concatenate([synth.kv_cache("kv_h256", t, seed=synth.DEFAULT_SEED + c) for t in ("K", "V")], axis=0)
+        kv = to_device(torch, dev, host)
+        p, n = wq.hlwq_kv_quantize(kv, n_residual=n_residual)
+        out = kv.clone()
+        sets.append((kv, p, n, out))
     state = {"i": 0}
     B, H, T, D = synth.CONFIGS["kv_h256"]["K"][1]
     tq = T - n_residual
     elems = 2 * B * H * tq * D
 
     def quant():
-        for kv, p, n, _ in sets[state["i"] % copies]:
-            wq.hlwq_kv_quantize(kv, n_residual=n_residual, packed=p, norms=n)
+        kv, p, n, _ = sets[state["i"] % copies]
+        wq.hlwq_kv_quantize(kv, n_residual=n_residual, packed=p, norms=n)
 
     def dequant():
-        for _, p, n, out in sets[state["i"] % copies]:
-            wq.hlwq_kv_dequantize(p, n, out, n_residual=n_residual)
+        _, p, n, out = sets[state["i"] % copies]
+        wq.hlwq_kv_dequantize(p, n, out, n_residual=n_residual)
         state["i"] += 1
 
     return {
@@ -174,7 +173,7 @@ def kv_workload(torch, wq, dev, copies=2, n_residual=128):
         "weights": elems,
         "bytes": elems * 2 + 2 * B * H * tq * (96 + 2),
         "kernels": ("hlwq_kv_quantize_kernel", "hlwq_kv_dequantize_kernel"),
-        "launches": 2,
+        "launches": 1,
         "keep": sets,
     }
 

@@ -285,23 +285,24 @@ def test_dense_5120_full_sampled_rows(wq, bits):
 
 
 def test_kv_h256_full(wq):
-    for t in ("K", "V"):
-        kv = synth.kv_cache("kv_h256", t)
-        _say("kv_h256", t, kv.shape)
-        dev = to_dev(kv)
-        packed, norms = wq.hlwq_kv_quantize(dev, n_residual=128)
-        out = torch.empty_like(dev)
-        out[:, :, -128:] = dev[:, :, -128:]
-        wq.hlwq_kv_dequantize(packed, norms, out, n_residual=128)
-        torch.cuda.synchronize()
-        assert torch.equal(out[:, :, -128:], dev[:, :, -128:])
-        for h, t0 in ((0, 0), (1, 12345), (3, 32640 - 512)):
-            sl = kv[:, h:h + 1, t0:t0 + 512]
-            op, on = ref.kv_quantize_c(np.concatenate([sl, np.zeros((1, 1, 128, 256), np.uint16)], axis=2),
-                                       n_residual=128)
-            assert np.array_equal(packed[:, h:h + 1, t0:t0 + 512].cpu().numpy(), op)
-            assert np.array_equal(f16_bits(norms[:, h:h + 1, t0:t0 + 512]), on.view(np.uint16))
-            assert np.array_equal(bf16_bits(out[:, h:h + 1, t0:t0 + 512]), ref.kv_dequantize_c(op, on))
+    # K and V stacked as one [2, 4, 32768, 256] tensor and encoded by one
+    # launch, as the benchmark does
+    kv = np.concatenate([synth.kv_cache("kv_h256", t) for t in ("K", "V")], axis=0)
+    _say("kv_h256 K+V", kv.shape)
+    dev = to_dev(kv)
+    packed, norms = wq.hlwq_kv_quantize(dev, n_residual=128)
+    out = torch.empty_like(dev)
+    out[:, :, -128:] = dev[:, :, -128:]
+    wq.hlwq_kv_dequantize(packed, norms, out, n_residual=128)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:, :, -128:], dev[:, :, -128:])
+    for bh, h, t0 in ((0, 0, 0), (0, 1, 12345), (1, 2, 777), (1, 3, 32640 - 512)):
+        sl = kv[bh:bh + 1, h:h + 1, t0:t0 + 512]
+        op, on = ref.kv_quantize_c(np.concatenate([sl, np.zeros((1, 1, 128, 256), np.uint16)], axis=2),
+                                   n_residual=128)
+        assert np.array_equal(packed[bh:bh + 1, h:h + 1, t0:t0 + 512].cpu().numpy(), op)
+        assert np.array_equal(f16_bits(norms[bh:bh + 1, h:h + 1, t0:t0 + 512]), on.view(np.uint16))
+        assert np.array_equal(bf16_bits(out[bh:bh + 1, h:h + 1, t0:t0 + 512]), ref.kv_dequantize_c(op, on))
 
 
 # --------------------------------------------------------------------------
