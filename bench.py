@@ -90,26 +90,38 @@ def stored_traffic(config, bits):
         return None
 
 
+# Working sets below this many bytes are held in two copies, and dequantize
+# reads the copy that quantize did not just write, so its input comes from HBM
+# and not from the 256 MB memory-side cache.
+_CACHE_SAFE_BYTES = 1 << 30
+
+
 def copy_ceiling(torch, dev, nbytes, reps=10):
     """Device-to-device copy moving the same number of bytes (half read, half
-    written) as one quantize or dequantize launch: a practical HBM ceiling."""
+    written) as one quantize or dequantize launch: a practical HBM ceiling.
+    Below 1 GiB the copy rotates over several buffer pairs, so it streams from
+    HBM and not from the memory-side cache."""
     n = max(nbytes // 8, 1 << 20)
-    src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
-    dst = torch.empty_like(src)
-    for _ in range(3):
+    pairs = max(1, min(16, -(-_CACHE_SAFE_BYTES // (8 * n))))
+    bufs = []
+    for _ in range(pairs):
+        src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        bufs.append((src, torch.empty_like(src)))
+    for src, dst in bufs:
         dst.copy_(src)
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()
-    for _ in range(reps):
+    for r in range(reps):
+        src, dst = bufs[r % pairs]
         dst.copy_(src)
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / reps
-    moved = 2 * src.numel() * 4
-    del src, dst
-    return {"gbs": round(moved / (ms * 1e-3) / 1e9, 1), "bytes": moved, "ms": round(ms, 4),
+    moved = 2 * n * 4
+    del bufs
+    return {"gbs": round(moved / (ms * 1e-3) / 1e9, 1), "bytes": moved, "ms": round(ms, 4), "buffer_pairs": pairs,
             "kernel": "torch copy_ (float32 device-to-device)"}
 
 
@@ -120,32 +132,50 @@ def to_device(torch, dev, bits_u16):
 def weight_workload(torch, wq, dev, config, bits):
     tensors = list(synth.CONFIGS[config])
     shapes = []
-    qitems, ditems = [], []
     for t in tensors:
         shape = synth.CONFIGS[config][t][1]
-        E, out, n_in = shape if len(shape) == 3 else (1, *shape)
-        shapes.append((E, out, n_in))
-        w = to_device(torch, dev, synth.weight(config, t))
-        nb = -(-n_in // 128)
-        lead = (E, out) if len(shape) == 3 else (out,)
-        p = torch.empty(lead + (nb, 16 * bits), dtype=torch.uint8, device=dev)
-        n = torch.empty(lead + (nb,), dtype=torch.float16, device=dev)
-        qitems.append((w, p, n))
-        ditems.append((torch.empty_like(w), p, n))
+        shapes.append((shape if len(shape) == 3 else (1, *shape)))
+    nbytes = algorithmic_bytes(shapes, bits)
+    copies = 1 if nbytes >= _CACHE_SAFE_BYTES else 2
+    sets = []
+    for c in range(copies):
+        qitems, ditems = [], []
+        for t, (E, out, n_in) in zip(tensors, shapes):
+            shape = synth.CONFIGS[config][t][1]
+            w = to_device(torch, dev, synth.weight(config, t, seed=synth.DEFAULT_SEED + c))
+            nb = -(-n_in // 128)
+            lead = (E, out) if len(shape) == 3 else (out,)
+            p = torch.empty(lead + (nb, 16 * bits), dtype=torch.uint8, device=dev)
+            n = torch.empty(lead + (nb,), dtype=torch.float16, device=dev)
+            qitems.append((w, p, n))
+            ditems.append((torch.empty_like(w), p, n))
+        wq.hlwq_quantize_grouped(qitems, bits)
+        sets.append((qitems, ditems))
+    state = {"i": 0}
+
+    def quant():
+        wq.hlwq_quantize_grouped(sets[state["i"] % copies][0], bits)
+
+    def dequant():
+        wq.hlwq_dequantize_grouped(sets[(state["i"] + 1) % copies][1], bits)
+        state["i"] += 1
+
     return {
-        "quantize": lambda: wq.hlwq_quantize_grouped(qitems, bits),
-        "dequantize": lambda: wq.hlwq_dequantize_grouped(ditems, bits),
+        "quantize": quant,
+        "dequantize": dequant,
         "weights": sum(E * o * i for E, o, i in shapes),
-        "bytes": algorithmic_bytes(shapes, bits),
+        "bytes": nbytes,
         "kernels": (f"hlwq_quantize_kernel<{bits}>", f"hlwq_dequantize_kernel<{bits}>"),
         "launches": 1,
-        "keep": (qitems, ditems),
+        "copies": copies,
+        "keep": sets,
     }
 
 
 def kv_workload(torch, wq, dev, copies=2, n_residual=128):
     """K and V of the cache held as one tensor [2 * batch, heads, tokens, 256]
-    (K first), so one launch encodes (or decodes) both."""
+    (K first), so one launch encodes (or decodes) both; two copies, and
+    dequantize reads the copy that quantize did not just write."""
     sets = []
     for c in range(copies):
         host = np.concatenate([synth.kv_cache("kv_h256", t, seed=synth.DEFAULT_SEED + c) for t in ("K", "V")], axis=0)
@@ -163,7 +193,7 @@ def kv_workload(torch, wq, dev, copies=2, n_residual=128):
         wq.hlwq_kv_quantize(kv, n_residual=n_residual, packed=p, norms=n)
 
     def dequant():
-        _, p, n, out = sets[state["i"] % copies]
+        _, p, n, out = sets[(state["i"] + 1) % copies]
         wq.hlwq_kv_dequantize(p, n, out, n_residual=n_residual)
         state["i"] += 1
 
@@ -174,6 +204,7 @@ def kv_workload(torch, wq, dev, copies=2, n_residual=128):
         "bytes": elems * 2 + 2 * B * H * tq * (96 + 2),
         "kernels": ("hlwq_kv_quantize_kernel", "hlwq_kv_dequantize_kernel"),
         "launches": 1,
+        "copies": copies,
         "keep": sets,
     }
 
@@ -252,8 +283,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: the HLWQ path shards by expert / row with no exchange, "
-              "and multi-GPU runs are not part of this build; use --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the HLWQ path shards by expert, row or head with no "
+              "exchange step, so one GPU's throughput is the per-GPU figure; use --gpus 1", file=sys.stderr)
         sys.exit(2)
     config = args.config
     bits = args.bits if args.bits is not None else (3 if config == "kv_h256" else 5)
@@ -335,12 +366,14 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": DESCRIPTIONS[config], "name": config, "weights": weights, "bits": bits,
-                   "block": 256 if config == "kv_h256" else 128},
+                   "block": 256 if config == "kv_h256" else 128, "input_sets": wl["copies"]},
         "hbm_gbs": round(step_gbs, 1),
         "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
-        "quantize": {"ms": round(float(q_ms.mean()), 4), "ms_min": round(float(q_ms.min()), 4),
+        "quantize": {"ms": round(float(q_ms.mean()), 4), "ms_median": round(float(np.median(q_ms)), 4),
+                     "ms_min": round(float(q_ms.min()), 4), "ms_max": round(float(q_ms.max()), 4),
                      "gbs": round(q_gbs, 1), "weights_per_s": weights / (q_ms.mean() * 1e-3)},
-        "dequantize": {"ms": round(float(d_ms.mean()), 4), "ms_min": round(float(d_ms.min()), 4),
+        "dequantize": {"ms": round(float(d_ms.mean()), 4), "ms_median": round(float(np.median(d_ms)), 4),
+                       "ms_min": round(float(d_ms.min()), 4), "ms_max": round(float(d_ms.max()), 4),
                        "gbs": round(d_gbs, 1), "weights_per_s": weights / (d_ms.mean() * 1e-3)},
         "roofline": roofline,
     }
