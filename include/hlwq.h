@@ -71,7 +71,7 @@ extern "C" {
 enum {
   HLWQ_OK = 0,
   HLWQ_ERR_NULL = -1,    /* a required pointer is NULL */
-  HLWQ_ERR_SHAPE = -2,   /* negative size, or a size whose byte count overflows int64 */
+  HLWQ_ERR_SHAPE = -2,   /* negative size, a size whose byte count overflows int64, or too small a capacity */
   HLWQ_ERR_BITS = -3,    /* bits not supported for this call */
   HLWQ_ERR_BLOCK = -4,   /* block != 128 (weights) or head_dim != 256 (KV) */
   HLWQ_ERR_DEVICE = -5,  /* the HIP launch reported an error */
@@ -119,10 +119,12 @@ int hlwq_dequantize_grouped(const hlwq_mat_desc* mats, int n, int bits, void* hi
 
 /* Quantize a KV cache [batch][heads][tokens][head_dim] (bf16) per head
  * vector: H256 rotation, 8 Lloyd-Max centroids, 3-bit codes ("Qwopus3.6-27B-v2
- * · HLWQ Q5", "Methodology notes", KV bullet).  head_dim must be 256 and bits
- * 3.  Tokens t < tokens - n_residual are encoded into packed
- * [batch][heads][tq][96] and norms [batch][heads][tq]; the newest n_residual
- * tokens (the unquantised residual window, 128 on that card) are not read. */
+ * · HLWQ Q5", "Methodology notes", KV bullet), or with bits = 2 the 4-centroid
+ * variant ("Qwen3.6-35B-A3B — HLWQ Q5", "Speed Benchmarks": Q3 and Q2 KV).
+ * head_dim must be 256 and bits 3 or 2.  Tokens t < tokens - n_residual are
+ * encoded into packed [batch][heads][tq][32 * bits] and norms
+ * [batch][heads][tq]; the newest n_residual tokens (the unquantised residual
+ * window, 128 on that card) are not read. */
 int hlwq_kv_quantize(const void* kv_bf16, int64_t batch, int64_t heads, int64_t tokens,
                      int head_dim, int bits, int64_t n_residual,
                      void* packed_u8, void* norms_f16, void* hip_stream);
@@ -134,6 +136,28 @@ int hlwq_kv_dequantize(const void* packed_u8, const void* norms_f16, int64_t bat
                        int64_t heads, int64_t tokens, int head_dim, int bits,
                        int64_t n_residual, void* kv_bf16_out, void* hip_stream);
 
+/* Append n_new tokens new_kv [batch][heads][n_new][head_dim] (bf16) to a
+ * streaming KV cache that holds `tokens` tokens, as a generation loop does
+ * ("Qwopus3.6-27B-v2 · HLWQ Q5", "Methodology notes", KV bullet: recent
+ * tokens stay unquantised in a residual buffer; "Qwen3.6-35B-A3B — HLWQ Q5",
+ * "Speed Benchmarks": Q3 / Q2 KV in a manual generation loop).  The cache:
+ *   window  bf16 [batch][heads][n_residual][head_dim], a ring: token t sits in
+ *           slot t mod n_residual while it is one of the newest n_residual;
+ *   packed  u8   [batch][heads][capacity][32 * bits] and
+ *   norms   fp16 [batch][heads][capacity]: token t's codes and norm at index t
+ *           once it has left the window.
+ * Afterwards tokens [0, tokens + n_new - n_residual) are encoded (exactly as
+ * hlwq_kv_quantize encodes them) and the newest min(tokens + n_new,
+ * n_residual) tokens are in the window; the call writes only the codes of the
+ * tokens that leave the window during it and the ring slots of the new tokens
+ * that stay.  head_dim 256, bits 3 or 2.  capacity must be at least
+ * tokens + n_new - n_residual whenever a token leaves the window; window may
+ * be NULL when n_residual = 0.  new_kv, window and packed must be 16-byte
+ * aligned.  n_new = 0 or batch * heads = 0 does nothing. */
+int hlwq_kv_append(const void* new_kv_bf16, int64_t batch, int64_t heads, int64_t n_new, int64_t tokens,
+                   void* window_bf16, int64_t n_residual, void* packed_u8, void* norms_f16, int64_t capacity,
+                   int head_dim, int bits, void* hip_stream);
+
 /* Bytes of packed codes for `rows` rows of `in` columns: rows * nb * block * bits / 8.
  * Returns 0 for invalid arguments. */
 size_t hlwq_packed_bytes(int64_t rows, int64_t in, int block, int bits);
@@ -142,7 +166,7 @@ size_t hlwq_packed_bytes(int64_t rows, int64_t in, int block, int bits);
 size_t hlwq_norm_count(int64_t rows, int64_t in, int block);
 
 /* Copy the fp32 codebook the kernels use: 2^bits centroids (ascending) and
- * 2^bits - 1 decision thresholds.  bits = 5 or 3.  Host-only, no GPU needed. */
+ * 2^bits - 1 decision thresholds.  bits = 5, 3 or 2.  Host-only, no GPU needed. */
 int hlwq_centroids(int bits, float* centroids, float* thresholds);
 
 /* Copy the two tables the kernels use to find a code with one compare.  For
@@ -153,7 +177,7 @@ int hlwq_centroids(int bits, float* centroids, float* thresholds);
  * times the number of thresholds below the 1/8-wide bucket k; at that byte
  * offset the entry table holds {fp32 bits of threshold b (+inf for the last),
  * b}, and the code is b + (y > threshold b).  kind 0: Q5 weights, 1: Q3
- * weights, 2: Q3 KV.  Copies at most `capacity` bucket bytes into `buckets`
+ * weights, 2: Q3 KV, 3: Q2 KV.  Copies at most `capacity` bucket bytes into `buckets`
  * and the 2 * 2^bits entry words into `entries` (either may be NULL), stores
  * scale and bias_bits, and returns the bucket count, or a negative status.
  * Host-only; exposed so the tables can be verified. */

@@ -18,7 +18,11 @@ the stored norm, round to bf16 ("Qwopus3.6-27B-v2 · HLWQ Q5", "Pipeline":
 dequantize per Linear to BF16).  The Q3 variant uses 8 centroids and packs
 8 codes into 3 bytes.  The KV-cache path ("Qwopus3.6-27B-v2 · HLWQ Q5",
 "Methodology notes", KV bullet) rotates every 256-wide head vector by H256, uses
-8 centroids and 3-bit codes, and leaves the newest 128 tokens unquantised.
+8 centroids and 3-bit codes, and leaves the newest 128 tokens unquantised; the
+2-bit variant uses 4 centroids ("Qwen3.6-35B-A3B — HLWQ Q5", "Speed
+Benchmarks": Q3 and Q2 KV).  During generation the cache is streamed: each new
+token enters the unquantised window and the token it pushes out is encoded
+(``kv_stream_c``).
 
 Two tiers:
 
@@ -51,6 +55,7 @@ the low bits of the first byte.
 """
 from __future__ import annotations
 
+import collections
 import math
 
 import numpy as np
@@ -320,3 +325,33 @@ def kv_dequantize_c(packed: np.ndarray, n16: np.ndarray, bits: int = 3, tables=N
     """Inverse of kv_quantize_c: -> bf16 bits [B, H, Tq, 256]."""
     codes = unpack_codes(packed, bits)
     return f32_to_bf16_rne(dequantize_vectors_c(codes, n16, bits, tables))
+
+
+def kv_stream_c(chunks, n_residual: int = 128, bits: int = 3, tables=None):
+    """Tier C streaming KV cache, token by token.
+
+    Tokens arrive in chunks (bf16 bits [B, H, n, 256] each).  Every arriving
+    token enters the window of the newest n_residual tokens, which are kept
+    unquantised ("Qwopus3.6-27B-v2 · HLWQ Q5", "Methodology notes": a residual
+    buffer holds recent tokens unquantised); when the window overflows, its
+    oldest token leaves and is encoded.  Returns (packed [B, H, Tq, 32 * bits],
+    norms [B, H, Tq], window [B, H, min(T, n_residual), 256] oldest first).
+    """
+    window = collections.deque()
+    packed, norms = [], []
+    shape = None
+    for chunk in chunks:
+        chunk = np.asarray(chunk, dtype=np.uint16)
+        shape = chunk.shape[:2]
+        for j in range(chunk.shape[2]):
+            window.append(chunk[:, :, j, :])
+            if len(window) > n_residual:
+                old = bf16_to_f32(window.popleft())
+                codes, _, n16, _ = quantize_vectors_c(old, bits, tables)
+                packed.append(pack_codes(codes, bits))
+                norms.append(n16)
+    B, H = shape
+    out_p = np.stack(packed, axis=2) if packed else np.zeros((B, H, 0, 32 * bits), np.uint8)
+    out_n = np.stack(norms, axis=2) if norms else np.zeros((B, H, 0), np.float16)
+    out_w = np.stack(list(window), axis=2) if window else np.zeros((B, H, 0, KV_DIM), np.uint16)
+    return out_p, out_n, out_w

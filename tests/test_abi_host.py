@@ -23,7 +23,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = wq.declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     raw = ctypes.CDLL(wq.binding.LIB_PATH)
     for name in names:
         assert hasattr(raw, name), name
@@ -51,7 +51,7 @@ def _bucket_codes(buckets, entries, scale, bias, y):
     return entries[e // 8, 1].astype(np.int64) + (y > thr)
 
 
-@pytest.mark.parametrize("kind,bits,limit", [(0, 5, 127.875), (1, 3, 127.875), (2, 3, 255.875)])
+@pytest.mark.parametrize("kind,bits,limit", [(0, 5, 127.875), (1, 3, 127.875), (2, 3, 255.875), (3, 2, 255.875)])
 def test_bucket_table_reproduces_threshold_count(kind, bits, limit):
     # The kernels find codes with two table reads and one compare; on every
     # fp32 value near a threshold or a bucket edge, and on a dense sweep of the
@@ -143,6 +143,7 @@ def test_kv_argument_errors(lib):
     kq, kd = lib.hlwq_kv_quantize, lib.hlwq_kv_dequantize
     assert kq(A, 1, 4, 300, 128, 3, 128, A, A, None) == EBLOCK
     assert kq(A, 1, 4, 300, 256, 5, 128, A, A, None) == EBITS
+    assert kq(A, 1, 4, 300, 256, 4, 128, A, A, None) == EBITS
     assert kq(A, 1, 4, -1, 256, 3, 128, A, A, None) == ESHAPE
     assert kq(A, 1, 4, 300, 256, 3, -1, A, A, None) == ESHAPE
     assert kq(None, 1, 4, 300, 256, 3, 128, A, A, None) == ENULL
@@ -153,3 +154,26 @@ def test_kv_argument_errors(lib):
     # every token inside the residual window: nothing to do
     assert kq(None, 1, 4, 128, 256, 3, 128, None, None, None) == OK
     assert kd(None, None, 1, 4, 100, 256, 3, 128, None, None) == OK
+
+
+def test_kv_append_argument_errors(lib):
+    A = 0x100000
+    ap = lib.hlwq_kv_append
+    # new_kv, batch, heads, n_new, tokens, window, n_res, packed, norms, capacity, head_dim, bits, stream
+    assert ap(A, 1, 4, 1, 500, A, 128, A, A, 400, 128, 3, None) == EBLOCK
+    assert ap(A, 1, 4, 1, 500, A, 128, A, A, 400, 256, 5, None) == EBITS
+    assert ap(A, 1, 4, -1, 500, A, 128, A, A, 400, 256, 3, None) == ESHAPE
+    assert ap(A, 1, 4, 1, -5, A, 128, A, A, 400, 256, 3, None) == ESHAPE
+    assert ap(A, 1, 4, 1, 500, A, -1, A, A, 400, 256, 3, None) == ESHAPE
+    # token 372 leaves the window: capacity must reach 373
+    assert ap(A, 1, 4, 1, 500, A, 128, A, A, 372, 256, 3, None) == ESHAPE
+    assert ap(None, 1, 4, 1, 500, A, 128, A, A, 400, 256, 3, None) == ENULL
+    assert ap(A, 1, 4, 1, 500, None, 128, A, A, 400, 256, 3, None) == ENULL
+    assert ap(A, 1, 4, 1, 500, A, 128, None, A, 400, 256, 3, None) == ENULL
+    assert ap(A + 8, 1, 4, 1, 500, A, 128, A, A, 400, 256, 3, None) == EALIGN
+    assert ap(A, 1, 4, 1, 500, A + 8, 128, A, A, 400, 256, 3, None) == EALIGN
+    assert ap(A, 1, 4, 1, 500, A, 128, A + 8, A, 400, 256, 3, None) == EALIGN
+    assert ap(A, 1, 4, 1, 500, A, 128, A, A + 1, 400, 256, 2, None) == EALIGN
+    # nothing to append, or nobody to append to
+    assert ap(None, 1, 4, 0, 500, None, 128, None, None, 0, 256, 3, None) == OK
+    assert ap(None, 0, 4, 3, 500, None, 128, None, None, 0, 256, 3, None) == OK

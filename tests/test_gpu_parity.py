@@ -204,6 +204,63 @@ def test_kv_cache_small(wq, shape):
     assert np.all(got[:, :, tq:] == 0x3F80), "residual window must stay untouched"
 
 
+@pytest.mark.parametrize("shape", [(1, 2, 300), (2, 3, 129), (1, 1, 1000)])
+def test_kv_cache_q2(wq, shape):
+    B, H, T = shape
+    kv = synth.random_bf16((B, H, T, 256), seed=T + 2, sigma=1.0)
+    _say("kv q2", shape)
+    dev = to_dev(kv)
+    packed, norms = wq.hlwq_kv_quantize(dev, n_residual=128, bits=2)
+    out = to_dev(np.full((B, H, T, 256), 0x3F80, np.uint16))
+    wq.hlwq_kv_dequantize(packed, norms, out, n_residual=128, bits=2)
+    torch.cuda.synchronize()
+    op, on = ref.kv_quantize_c(kv, n_residual=128, bits=2)
+    assert np.array_equal(packed.cpu().numpy(), op)
+    assert np.array_equal(f16_bits(norms), on.view(np.uint16))
+    tq = max(T - 128, 0)
+    got = bf16_bits(out)
+    assert np.array_equal(got[:, :, :tq], ref.kv_dequantize_c(op, on, bits=2))
+    assert np.all(got[:, :, tq:] == 0x3F80)
+
+
+def _append_case(wq, B, H, chunks, n_res, bits, seed, extra=3):
+    """Stream `chunks` tokens through hlwq_kv_append and compare the cache with
+    the oracle's token-by-token stream after the last call."""
+    T = sum(chunks)
+    kv = synth.random_bf16((B, H, T, 256), seed=seed, sigma=1.0)
+    cap = max(T - n_res, 0) + extra
+    packed = torch.full((B, H, cap, 32 * bits), 0xAB, dtype=torch.uint8, device="cuda")
+    norms = torch.full((B, H, cap), 7.0, dtype=torch.float16, device="cuda")
+    window = to_dev(np.full((B, H, n_res, 256), 0x3F80, np.uint16)) if n_res else None
+    tokens, parts = 0, []
+    for n in chunks:
+        part = kv[:, :, tokens:tokens + n]
+        parts.append(part)
+        tokens = wq.hlwq_kv_append(to_dev(part), window, packed, norms, tokens, n_residual=n_res, bits=bits)
+    torch.cuda.synchronize()
+    op, on, ow = ref.kv_stream_c(parts, n_residual=n_res, bits=bits)
+    tq = op.shape[2]
+    got_p, got_n = packed.cpu().numpy(), f16_bits(norms)
+    assert np.array_equal(got_p[:, :, :tq], op)
+    assert np.array_equal(got_n[:, :, :tq], on.view(np.uint16))
+    assert np.all(got_p[:, :, tq:] == 0xAB), "codes past the encoded tokens must stay untouched"
+    assert np.all(got_n[:, :, tq:] == np.float16(7.0).view(np.uint16))
+    if n_res:
+        w = bf16_bits(window)
+        kept = ow.shape[2]
+        for i in range(kept):
+            t = T - kept + i
+            assert np.array_equal(w[:, :, t % n_res], ow[:, :, i]), f"ring slot of token {t}"
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+@pytest.mark.parametrize("chunks,n_res", [((1,) * 150, 128), ((100, 1, 1, 60, 3, 200, 1), 128), ((300,), 128),
+                                          ((5, 40, 1), 0), ((3, 1, 2, 70), 1), ((33, 64, 31, 1), 32)])
+def test_kv_append_matches_token_stream(wq, bits, chunks, n_res):
+    _say("kv append", bits, chunks[:8], n_res)
+    _append_case(wq, 2, 3, chunks, n_res, bits, seed=len(chunks) * 10 + n_res + bits)
+
+
 def test_kv_cache_underflow_vectors(wq):
     f = synth.f32_to_bf16_bits
     kv = synth.random_bf16((1, 2, 200, 256), seed=77, sigma=1.0)

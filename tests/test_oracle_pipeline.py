@@ -199,3 +199,49 @@ def test_underflowing_squares_reach():
         assert abs(float(y[0, 0]) - (1.5 + (L - 1) * 255 / 256) * 2.0 ** -0.5) < 1e-3 * L
         assert np.abs(y).max() < math.sqrt(L * (1 + rounds / 2))
         assert codes[0, 0] == (1 << bits) - 1
+
+
+def test_kv_stream_hand_example():
+    # window of 2: tokens a, b, c, d arrive one by one; a and b leave (in that
+    # order) and are encoded, c and d stay unquantised
+    toks = synth.random_bf16((1, 1, 4, 256), seed=21, sigma=1.0)
+    packed, norms, window = ref.kv_stream_c([toks[:, :, i:i + 1] for i in range(4)], n_residual=2)
+    assert packed.shape == (1, 1, 2, 96) and norms.shape == (1, 1, 2)
+    assert np.array_equal(window, toks[:, :, 2:])
+    for i in range(2):
+        codes, _, n16, _ = ref.quantize_vectors_c(ref.bf16_to_f32(toks[:, :, i]), 3)
+        assert np.array_equal(packed[:, :, i], ref.pack_codes(codes, 3))
+        assert np.array_equal(norms[:, :, i].view(np.uint16), n16.view(np.uint16))
+    # a window of 0 encodes every token on arrival
+    p0, n0, w0 = ref.kv_stream_c([toks], n_residual=0)
+    assert p0.shape[2] == 4 and w0.shape[2] == 0
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+@pytest.mark.parametrize("chunks", [(1,) * 40, (7, 1, 30, 2), (200,), (130, 3, 5)])
+def test_kv_stream_equals_static_cache(bits, chunks):
+    # however the tokens arrive, the streamed cache is the static one: every
+    # token but the newest n_residual encoded, the newest kept as they came
+    T = sum(chunks)
+    kv = synth.random_bf16((2, 2, T, 256), seed=T + bits, sigma=1.0)
+    n_res = 16
+    parts, t = [], 0
+    for n in chunks:
+        parts.append(kv[:, :, t:t + n])
+        t += n
+    packed, norms, window = ref.kv_stream_c(parts, n_residual=n_res, bits=bits)
+    sp, sn = ref.kv_quantize_c(kv, n_residual=n_res, bits=bits)
+    assert np.array_equal(packed, sp)
+    assert np.array_equal(norms.view(np.uint16), sn.view(np.uint16))
+    assert np.array_equal(window, kv[:, :, max(T - n_res, 0):])
+
+
+def test_kv_q2_quality():
+    # 4 Lloyd-Max levels: cosine near sqrt(1 - D_4), D_4 = 0.1175 (Max, 1960)
+    kv = synth.random_bf16((1, 2, 300, 256), seed=31, sigma=1.0)
+    packed, n16 = ref.kv_quantize_c(kv, n_residual=128, bits=2)
+    assert packed.shape == (1, 2, 172, 64)
+    out = ref.bf16_to_f32(ref.kv_dequantize_c(packed, n16, bits=2)).astype(np.float64)
+    x = ref.bf16_to_f32(kv[:, :, :172]).astype(np.float64)
+    c = float(np.mean(np.sum(x * out, -1) / np.linalg.norm(x, axis=-1) / np.linalg.norm(out, axis=-1)))
+    assert abs(c - math.sqrt(1 - 0.1175)) < 5e-3

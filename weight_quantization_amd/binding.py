@@ -52,6 +52,7 @@ _SIGNATURES = {
     "hlwq_dequantize_grouped": (_int, [ctypes.POINTER(MatDesc), _int, _int, _vp]),
     "hlwq_kv_quantize": (_int, [_vp, _i64, _i64, _i64, _int, _int, _i64, _vp, _vp, _vp]),
     "hlwq_kv_dequantize": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _i64, _vp, _vp]),
+    "hlwq_kv_append": (_int, [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _int, _int, _vp]),
     "hlwq_packed_bytes": (ctypes.c_size_t, [_i64, _i64, _int, _int]),
     "hlwq_norm_count": (ctypes.c_size_t, [_i64, _i64, _int]),
     "hlwq_search_table": (_int, [_int, ctypes.POINTER(ctypes.c_uint8), _int, ctypes.POINTER(ctypes.c_uint32),
@@ -124,7 +125,7 @@ def hlwq_search_table(kind: int):
     n = lib.hlwq_search_table(kind, None, 0, None, ctypes.byref(scale), ctypes.byref(bias))
     if n < 0:
         _check("hlwq_search_table", n)
-    K = 32 if kind == 0 else 8
+    K = {0: 32, 1: 8, 2: 8, 3: 4}.get(kind, 8)
     buckets = (ctypes.c_uint8 * n)()
     entries = (ctypes.c_uint32 * (2 * K))()
     lib.hlwq_search_table(kind, buckets, n, entries, ctypes.byref(scale), ctypes.byref(bias))
@@ -254,7 +255,8 @@ def hlwq_dequantize_grouped(items, bits: int = 5, stream=None):
 
 
 def hlwq_kv_quantize(kv, n_residual: int = 128, bits: int = 3, packed=None, norms=None, stream=None):
-    """Quantize a bf16 KV cache [B, H, T, 256]; returns (packed [B,H,Tq,96], norms [B,H,Tq])."""
+    """Quantize a bf16 KV cache [B, H, T, 256] (bits 3 or 2); returns
+    (packed [B, H, Tq, 32 * bits], norms [B, H, Tq])."""
     torch = _torch()
     _need(kv, torch.bfloat16, "kv")
     if kv.dim() != 4:
@@ -273,6 +275,33 @@ def hlwq_kv_quantize(kv, n_residual: int = 128, bits: int = 3, packed=None, norm
                                          _stream_handle(stream))
     _check("hlwq_kv_quantize", st)
     return packed, norms
+
+
+def hlwq_kv_append(new_kv, window, packed, norms, tokens: int, n_residual: int = 128, bits: int = 3, stream=None):
+    """Append new_kv [B, H, n_new, 256] to a streaming cache holding `tokens`
+    tokens: window [B, H, n_residual, 256] (ring, token t in slot
+    t % n_residual), packed [B, H, capacity, 32 * bits], norms [B, H, capacity]."""
+    torch = _torch()
+    _need(new_kv, torch.bfloat16, "new_kv")
+    if new_kv.dim() != 4:
+        raise ValueError("new_kv must be [batch, heads, n_new, head_dim]")
+    B, H, n_new, D = new_kv.shape
+    if window is not None:
+        _need(window, torch.bfloat16, "window")
+        if tuple(window.shape) != (B, H, n_residual, D):
+            raise ValueError("window shape mismatch")
+    elif n_residual:
+        raise ValueError("a window is needed when n_residual > 0")
+    _need(packed, torch.uint8, "packed")
+    _need(norms, torch.float16, "norms")
+    capacity = packed.shape[2]
+    if tuple(packed.shape) != (B, H, capacity, D * bits // 8) or tuple(norms.shape) != (B, H, capacity):
+        raise ValueError("packed / norms shape mismatch")
+    st = load_library().hlwq_kv_append(_ptr(new_kv), B, H, n_new, tokens, _ptr(window) if window is not None else None,
+                                       n_residual, _ptr(packed), _ptr(norms), capacity, D, bits,
+                                       _stream_handle(stream))
+    _check("hlwq_kv_append", st)
+    return tokens + n_new
 
 
 def hlwq_kv_dequantize(packed, norms, kv_out, n_residual: int = 128, bits: int = 3, stream=None):

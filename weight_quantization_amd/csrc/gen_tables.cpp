@@ -1,6 +1,7 @@
 // Build-time generator of the HLWQ codebook tables.
 //
-// Prints a C header (to stdout) with, for Q5 (K = 32) and Q3 (K = 8):
+// Prints a C header (to stdout) with, for Q5 (K = 32), Q3 (K = 8) and the
+// 2-bit KV variant (K = 4):
 //   * the Lloyd-Max centroids for N(0, 1), rounded to fp32, ascending
 //     (model card "Qwen3.6-35B-A3B — HLWQ Q5", section "Method", step [4];
 //     "Qwopus3.6-27B-v2 · HLWQ Q5", "Methodology notes": centroids computed for a
@@ -238,6 +239,7 @@ int main() {
   const Tables q5 = make_tables(32, 2048);
   const Tables q3 = make_tables(8, 2048);
   const Tables kv3 = make_tables(8, 4096);
+  const Tables kv2 = make_tables(4, 4096);
   std::printf("// Generated at build time by gen_tables.cpp: Lloyd-Max tables for N(0,1).\n");
   std::printf("#pragma once\n");
   std::printf("#define HLWQ_SEARCH_SCALE %af\n", (double)kScale);
@@ -252,5 +254,9 @@ int main() {
   emit_bytes("HLWQ_BUCKET_3", q3.bucket);
   emit_words("HLWQ_ENTRY_3", q3.entry);
   emit_bytes("HLWQ_KV_BUCKET_3", kv3.bucket);
+  emit_floats("HLWQ_CENTROIDS_2", kv2.cent);
+  emit_floats("HLWQ_THRESHOLDS_2", kv2.thr);
+  emit_words("HLWQ_ENTRY_2", kv2.entry);
+  emit_bytes("HLWQ_KV_BUCKET_2", kv2.bucket);
   return 0;
 }

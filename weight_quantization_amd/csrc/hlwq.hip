@@ -53,6 +53,9 @@ __constant__ uint32_t c_bucket3[HLWQ_BUCKETS / 4] = HLWQ_BUCKET_3;
 __constant__ uint32_t c_kvbucket3[HLWQ_KV_BUCKETS / 4] = HLWQ_KV_BUCKET_3;
 __constant__ uint32_t c_entry5[2 * 32] = HLWQ_ENTRY_5;
 __constant__ uint32_t c_entry3[2 * 8] = HLWQ_ENTRY_3;
+__constant__ float c_cent2[4] = HLWQ_CENTROIDS_2;
+__constant__ uint32_t c_entry2[2 * 4] = HLWQ_ENTRY_2;
+__constant__ uint32_t c_kvbucket2[HLWQ_KV_BUCKETS / 4] = HLWQ_KV_BUCKET_2;
 
 const float h_cent5[32] = HLWQ_CENTROIDS_5;
 const float h_thr5[31] = HLWQ_THRESHOLDS_5;
@@ -63,6 +66,10 @@ const uint32_t h_bucket3[HLWQ_BUCKETS / 4] = HLWQ_BUCKET_3;
 const uint32_t h_kvbucket3[HLWQ_KV_BUCKETS / 4] = HLWQ_KV_BUCKET_3;
 const uint32_t h_entry5[2 * 32] = HLWQ_ENTRY_5;
 const uint32_t h_entry3[2 * 8] = HLWQ_ENTRY_3;
+const float h_cent2[4] = HLWQ_CENTROIDS_2;
+const float h_thr2[3] = HLWQ_THRESHOLDS_2;
+const uint32_t h_entry2[2 * 4] = HLWQ_ENTRY_2;
+const uint32_t h_kvbucket2[HLWQ_KV_BUCKETS / 4] = HLWQ_KV_BUCKET_2;
 
 // ---------------------------------------------------------------------------
 // device helpers
@@ -635,7 +642,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 
 struct KvArgs {
   uint16_t* kv;       // [bh][tokens][256]
-  uint8_t* packed;    // [bh][tq][96]
+  uint8_t* packed;    // [bh][tq][32 * bits]
   uint16_t* norms;    // [bh][tq]
   int64_t tokens;
   uint32_t tq;        // quantised tokens per head
@@ -659,14 +666,25 @@ __device__ __forceinline__ KvPos kv_pos(const KvArgs& a, uint32_t b, int lane) {
   return p;
 }
 
+// KV kernels: BITS = 3 (8 centroids) or 2 (4 centroids); a vector's codes take
+// 32 * BITS bytes, 16 * BITS from each lane of its pair.
+template <int BITS>
+__device__ __forceinline__ void fill_kv_search(uint32_t* tab) {
+  const uint32_t* bucket = (BITS == 3) ? c_kvbucket3 : c_kvbucket2;
+  const uint32_t* entry = (BITS == 3) ? c_entry3 : c_entry2;
+  for (int i = threadIdx.x; i < HLWQ_KV_BUCKETS / 4; i += kThreads) tab[64 + i] = bucket[i];
+  if (threadIdx.x < 2 * (1 << BITS)) tab[threadIdx.x] = entry[threadIdx.x];
+}
+
+template <int BITS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_kv_quantize_kernel(const KvArgs a) {
   // entry table at offset 0, bucket table, per-wave stages
   constexpr int kTab = 256 + HLWQ_KV_BUCKETS;
+  constexpr uint32_t kVec = 32 * BITS;  // packed bytes per vector
   __shared__ __attribute__((aligned(256))) uint8_t lds[kTab + kWaves * kStage];
   uint32_t* tab = reinterpret_cast<uint32_t*>(lds);
   uint8_t* stage_all = lds + kTab;
-  for (int i = threadIdx.x; i < HLWQ_KV_BUCKETS / 4; i += kThreads) tab[64 + i] = c_kvbucket3[i];
-  if (threadIdx.x < 16) tab[threadIdx.x] = c_entry3[threadIdx.x];
+  fill_kv_search<BITS>(tab);
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -699,24 +717,26 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
     for (int j = 0; j < kBlock; ++j) x[j] = cross_pair(x[j], sgn);
 
-    uint32_t words[12];
-    encode<3, kBlock>(x, ni.r, lds, 256u, __uint_as_float(HLWQ_KV_BUCKET_BIAS), words);
+    uint32_t words[4 * BITS];
+    encode<BITS, kBlock>(x, ni.r, lds, 256u, __uint_as_float(HLWQ_KV_BUCKET_BIAS), words);
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
+    for (int q = 0; q < BITS; ++q) {
       const u32x4 v = {words[4 * q], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]};
-      *reinterpret_cast<u32x4*>(stage + 48 * lane + 16 * q) = v;
+      *reinterpret_cast<u32x4*>(stage + 16 * BITS * lane + 16 * q) = v;
     }
     const size_t vec0 = static_cast<size_t>(p.bh) * a.tq + p.t0;
-    stage_out<3, false>(a.packed + vec0 * 96, p.nvalid * 96u, stage, lane, sl);
+    stage_out<BITS, false>(a.packed + vec0 * kVec, p.nvalid * kVec, stage, lane, sl);
     if (p.half == 0 && (static_cast<uint32_t>(lane) >> 1) < p.nvalid) a.norms[vec0 + (lane >> 1)] = ni.n16;
   }
 }
 
+template <int BITS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_kv_dequantize_kernel(const KvArgs a) {
-  // centroid pair table at offset 0, then the per-wave stages
+  // centroid pair table at offset 0 (512 bytes at most), then the per-wave stages
+  constexpr uint32_t kVec = 32 * BITS;  // packed bytes per vector
   __shared__ __attribute__((aligned(256))) uint8_t lds[512 + kWaves * kStage];
   uint8_t* stage_all = lds + 512;
-  fill_pairs<3>(reinterpret_cast<float*>(lds), c_cent3);
+  fill_pairs<BITS>(reinterpret_cast<float*>(lds), (BITS == 3) ? c_cent3 : c_cent2);
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -729,15 +749,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     refresh(sl, lane_a);
     const KvPos p = kv_pos(a, b, lane);
     const size_t vec0 = static_cast<size_t>(p.bh) * a.tq + p.t0;
-    stage_in<3, false, 0>(a.packed + vec0 * 96, p.nvalid * 96u, stage, lane, sl);
+    stage_in<BITS, false, 0>(a.packed + vec0 * kVec, p.nvalid * kVec, stage, lane, sl);
     const float scale = f16_value(a.norms[vec0 + (p.t - p.t0)]) * 0x1p-8f;
     wait_vmem();
     // lanes past the end of the batch read (and later write) the last vector
     const uint32_t slot = 2u * (p.t - p.t0) + p.half;
-    uint32_t words[12];
+    uint32_t words[4 * BITS];
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + 48 * slot + 16 * q);
+    for (int q = 0; q < BITS; ++q) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + 16 * BITS * slot + 16 * q);
       words[4 * q] = v.x;
       words[4 * q + 1] = v.y;
       words[4 * q + 2] = v.z;
@@ -745,7 +765,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     }
 
     float v[kBlock];
-    decode_stage1<3, kBlock>(words, lds, v);
+    decode_stage1<BITS, kBlock>(words, lds, v);
     fwht<kBlock, 2>(v);
     // stride-128 stage across the lane pair, then scale and round to bf16
     const float sgn = pair_sign(p.half);
@@ -765,6 +785,101 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       write_staged_block(stage, (p.t - p.t0) * 2u * kKvDim + p.half * 2u * kBlock, kBlock, pk);
       stage_out<16, true>(dst, p.nvalid * 2u * kKvDim, stage, lane, sl);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming KV append: during generation every new token enters the bf16
+// window of the newest n_residual tokens (a ring: token t in slot
+// t mod n_residual), and the token it pushes out is encoded into the packed
+// cache.  One wave per job: job h < bh is head h's "window job" (encode the
+// leaving tokens that are still in the ring, then write the new tokens that
+// stay into the ring, in that order, so no slot is overwritten before it is
+// read); the other jobs encode, 32 at a time, leaving tokens that arrive and
+// leave within this call (read from the new tokens directly).
+// ---------------------------------------------------------------------------
+
+struct KvAppendArgs {
+  const uint16_t* src;  // new tokens [bh][n_new][256]
+  uint16_t* ring;       // window [bh][n_res][256]
+  uint8_t* packed;      // [bh][capacity][32 * bits]
+  uint16_t* norms;      // [bh][capacity]
+  int64_t tokens, n_new, n_res, capacity;
+  uint32_t bh;           // batch * heads
+  uint32_t window_jobs;  // bh if n_res > 0, else 0
+  uint32_t in_batches;   // per head: ceil(max(n_new - n_res, 0) / 32)
+};
+
+// Encode tokens o0 .. o0 + count - 1 (count <= 32) of head bhi: lane pair
+// v = lane / 2 takes token o0 + v (lanes past count repeat the last token and
+// store nothing), each lane one half of its 256 values.
+template <int BITS>
+__device__ __forceinline__ void append_encode(const KvAppendArgs& a, const uint8_t* __restrict__ lds, uint32_t bhi,
+                                              int64_t o0, uint32_t count, bool from_ring, int lane) {
+  constexpr uint32_t kVec = 32 * BITS;
+  const uint32_t v = static_cast<uint32_t>(lane) >> 1;
+  const uint32_t half = lane & 1;
+  const int64_t o = o0 + (v < count ? v : count - 1);
+  const uint16_t* p = from_ring ? a.ring + (static_cast<int64_t>(bhi) * a.n_res + o % a.n_res) * kKvDim
+                                : a.src + (static_cast<int64_t>(bhi) * a.n_new + (o - a.tokens)) * kKvDim;
+  float x[kBlock];
+  load_block(p + half * kBlock, kBlock, x);
+  const float s_half = sumsq_tree(x);
+  const NormInfo ni = norm_info(s_half + lane_xor1(s_half));
+  fwht(x);
+  const float sgn = pair_sign(half);
+#pragma unroll
+  for (int j = 0; j < kBlock; ++j) x[j] = cross_pair(x[j], sgn);
+  uint32_t words[4 * BITS];
+  encode<BITS, kBlock>(x, ni.r, lds, 256u, __uint_as_float(HLWQ_KV_BUCKET_BIAS), words);
+  if (v < count) {
+    const int64_t vec = static_cast<int64_t>(bhi) * a.capacity + o;
+    u32x4* dst = reinterpret_cast<u32x4*>(a.packed + vec * kVec + half * (kVec / 2));
+#pragma unroll
+    for (int q = 0; q < BITS; ++q) dst[q] = u32x4{words[4 * q], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]};
+    if (half == 0) a.norms[vec] = ni.n16;
+  }
+}
+
+template <int BITS>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) hlwq_kv_append_kernel(const KvAppendArgs a) {
+  __shared__ __attribute__((aligned(256))) uint8_t lds[256 + HLWQ_KV_BUCKETS];
+  fill_kv_search<BITS>(reinterpret_cast<uint32_t*>(lds));
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const uint32_t job = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t total = a.tokens + a.n_new;
+  const int64_t leave_end = total - a.n_res;  // tokens below this index are encoded afterwards
+  uint32_t bhi;
+  int64_t o_begin, o_end;
+  const bool window_job = job < a.window_jobs;
+  if (window_job) {
+    bhi = job;
+    o_begin = a.tokens > a.n_res ? a.tokens - a.n_res : 0;  // oldest token in the ring
+    o_end = leave_end < a.tokens ? leave_end : a.tokens;     // leaving tokens still in the ring
+  } else {
+    const uint32_t j = job - a.window_jobs;
+    if (j >= a.bh * a.in_batches) return;
+    bhi = j / a.in_batches;
+    o_begin = a.tokens + 32 * static_cast<int64_t>(j - bhi * a.in_batches);
+    o_end = o_begin + 32 < leave_end ? o_begin + 32 : leave_end;
+  }
+  for (int64_t o0 = o_begin; o0 < o_end; o0 += 32) {
+    const int64_t n = o_end - o0;
+    append_encode<BITS>(a, lds, bhi, o0, static_cast<uint32_t>(n < 32 ? n : 32), window_job, lane);
+  }
+  if (!window_job) return;
+  // every ring read above has returned before any slot is rewritten
+  wait_vmem();
+  // the new tokens that stay in the window: t in [max(tokens, total - n_res), total)
+  const int64_t t0 = leave_end > a.tokens ? leave_end : a.tokens;
+  const int64_t chunks = (total - t0) * (kKvDim / 8);  // 16-byte chunks
+  for (int64_t c = lane; c < chunks; c += 64) {
+    const int64_t t = t0 + c / (kKvDim / 8);
+    const int64_t k = c % (kKvDim / 8);
+    const u32x4 val = reinterpret_cast<const u32x4*>(a.src + (static_cast<int64_t>(bhi) * a.n_new + (t - a.tokens)) * kKvDim)[k];
+    reinterpret_cast<u32x4*>(a.ring + (static_cast<int64_t>(bhi) * a.n_res + t % a.n_res) * kKvDim)[k] = val;
   }
 }
 
@@ -885,7 +1000,7 @@ int make_single(const void* w, const void* packed, const void* norms, int64_t n_
 int run_kv(bool quant, const void* kv, void* packed, void* norms, int64_t batch, int64_t heads, int64_t tokens,
            int head_dim, int bits, int64_t n_residual, hipStream_t stream) {
   if (head_dim != kKvDim) return HLWQ_ERR_BLOCK;
-  if (bits != 3) return HLWQ_ERR_BITS;
+  if (bits != 3 && bits != 2) return HLWQ_ERR_BITS;
   if (batch < 0 || heads < 0 || tokens < 0 || n_residual < 0) return HLWQ_ERR_SHAPE;
   const int64_t tq = tokens > n_residual ? tokens - n_residual : 0;
   int64_t bh, nvec, elems, bytes;
@@ -909,8 +1024,58 @@ int run_kv(bool quant, const void* kv, void* packed, void* norms, int64_t batch,
   if (!mul_ok(bh, a.nbt, &batches) || batches > 0x7fffffff) return HLWQ_ERR_LIMIT;
   a.total_batches = static_cast<uint32_t>(batches);
   const dim3 grid(persistent_grid(a.total_batches)), block(kThreads);
-  if (quant) hipLaunchKernelGGL(hlwq_kv_quantize_kernel, grid, block, 0, stream, a);
-  else hipLaunchKernelGGL(hlwq_kv_dequantize_kernel, grid, block, 0, stream, a);
+  if (quant) {
+    if (bits == 3) hipLaunchKernelGGL(hlwq_kv_quantize_kernel<3>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(hlwq_kv_quantize_kernel<2>, grid, block, 0, stream, a);
+  } else {
+    if (bits == 3) hipLaunchKernelGGL(hlwq_kv_dequantize_kernel<3>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(hlwq_kv_dequantize_kernel<2>, grid, block, 0, stream, a);
+  }
+  return launch_status();
+}
+
+int run_kv_append(const void* src, int64_t batch, int64_t heads, int64_t n_new, int64_t tokens, void* ring,
+                  int64_t n_residual, void* packed, void* norms, int64_t capacity, int head_dim, int bits,
+                  hipStream_t stream) {
+  if (head_dim != kKvDim) return HLWQ_ERR_BLOCK;
+  if (bits != 3 && bits != 2) return HLWQ_ERR_BITS;
+  if (batch < 0 || heads < 0 || n_new < 0 || tokens < 0 || n_residual < 0 || capacity < 0) return HLWQ_ERR_SHAPE;
+  int64_t bh, total;
+  if (!mul_ok(batch, heads, &bh) || __builtin_add_overflow(tokens, n_new, &total)) return HLWQ_ERR_SHAPE;
+  if (bh == 0 || n_new == 0) return HLWQ_OK;
+  const int64_t leave_end = total - n_residual;                          // encoded tokens afterwards
+  const int64_t leave_begin = tokens > n_residual ? tokens - n_residual : 0;  // encoded tokens before
+  const bool encodes = leave_end > leave_begin;
+  if (!src || (n_residual > 0 && !ring) || (encodes && (!packed || !norms))) return HLWQ_ERR_NULL;
+  if (encodes && capacity < leave_end) return HLWQ_ERR_SHAPE;
+  int64_t elems, bytes, vecs;
+  if (!mul_ok(bh, n_new, &elems) || !mul_ok(elems, 2 * kKvDim, &bytes) || !mul_ok(bh, capacity, &vecs) ||
+      !mul_ok(bh, n_residual, &elems))
+    return HLWQ_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(src) & 15u) || (reinterpret_cast<uintptr_t>(ring) & 15u) ||
+      (reinterpret_cast<uintptr_t>(packed) & 15u) || (reinterpret_cast<uintptr_t>(norms) & 1u))
+    return HLWQ_ERR_ALIGN;
+  const int64_t in_leaving = n_new > n_residual ? n_new - n_residual : 0;
+  const int64_t in_batches = ceil_div(in_leaving, 32);
+  int64_t jobs;
+  if (bh > 0x3fffffff || !mul_ok(bh, in_batches, &jobs) || jobs > 0x3fffffff) return HLWQ_ERR_LIMIT;
+  KvAppendArgs a;
+  a.src = static_cast<const uint16_t*>(src);
+  a.ring = static_cast<uint16_t*>(ring);
+  a.packed = static_cast<uint8_t*>(packed);
+  a.norms = static_cast<uint16_t*>(norms);
+  a.tokens = tokens;
+  a.n_new = n_new;
+  a.n_res = n_residual;
+  a.capacity = capacity;
+  a.bh = static_cast<uint32_t>(bh);
+  a.window_jobs = n_residual > 0 ? static_cast<uint32_t>(bh) : 0u;
+  a.in_batches = static_cast<uint32_t>(in_batches);
+  const int64_t all_jobs = a.window_jobs + jobs;
+  if (all_jobs == 0) return HLWQ_OK;
+  const dim3 grid(static_cast<uint32_t>(ceil_div(all_jobs, kWaves))), block(kThreads);
+  if (bits == 3) hipLaunchKernelGGL(hlwq_kv_append_kernel<3>, grid, block, 0, stream, a);
+  else hipLaunchKernelGGL(hlwq_kv_append_kernel<2>, grid, block, 0, stream, a);
   return launch_status();
 }
 
@@ -959,6 +1124,13 @@ int hlwq_kv_dequantize(const void* packed_u8, const void* norms_f16, int64_t bat
                 tokens, head_dim, bits, n_residual, static_cast<hipStream_t>(hip_stream));
 }
 
+int hlwq_kv_append(const void* new_kv_bf16, int64_t batch, int64_t heads, int64_t n_new, int64_t tokens,
+                   void* window_bf16, int64_t n_residual, void* packed_u8, void* norms_f16, int64_t capacity,
+                   int head_dim, int bits, void* hip_stream) {
+  return run_kv_append(new_kv_bf16, batch, heads, n_new, tokens, window_bf16, n_residual, packed_u8, norms_f16,
+                       capacity, head_dim, bits, static_cast<hipStream_t>(hip_stream));
+}
+
 size_t hlwq_packed_bytes(int64_t rows, int64_t in, int block, int bits) {
   if (rows < 0 || in < 0 || block <= 0 || (block % 8) != 0 || bits <= 0 || bits > 8) return 0;
   int64_t nblk, bytes;
@@ -975,10 +1147,10 @@ size_t hlwq_norm_count(int64_t rows, int64_t in, int block) {
 }
 
 int hlwq_centroids(int bits, float* centroids, float* thresholds) {
-  if (bits != 5 && bits != 3) return HLWQ_ERR_BITS;
+  if (bits != 5 && bits != 3 && bits != 2) return HLWQ_ERR_BITS;
   const int K = 1 << bits;
-  const float* c = bits == 5 ? h_cent5 : h_cent3;
-  const float* t = bits == 5 ? h_thr5 : h_thr3;
+  const float* c = bits == 5 ? h_cent5 : bits == 3 ? h_cent3 : h_cent2;
+  const float* t = bits == 5 ? h_thr5 : bits == 3 ? h_thr3 : h_thr2;
   if (centroids) std::memcpy(centroids, c, sizeof(float) * K);
   if (thresholds) std::memcpy(thresholds, t, sizeof(float) * (K - 1));
   return HLWQ_OK;
@@ -994,6 +1166,7 @@ int hlwq_search_table(int kind, uint8_t* buckets, int capacity, uint32_t* entrie
     case 0: bucket = h_bucket5; entry = h_entry5; n = HLWQ_BUCKETS; K = 32; bias = HLWQ_BUCKET_BIAS; break;
     case 1: bucket = h_bucket3; entry = h_entry3; n = HLWQ_BUCKETS; K = 8; bias = HLWQ_BUCKET_BIAS; break;
     case 2: bucket = h_kvbucket3; entry = h_entry3; n = HLWQ_KV_BUCKETS; K = 8; bias = HLWQ_KV_BUCKET_BIAS; break;
+    case 3: bucket = h_kvbucket2; entry = h_entry2; n = HLWQ_KV_BUCKETS; K = 4; bias = HLWQ_KV_BUCKET_BIAS; break;
     default: return HLWQ_ERR_BITS;
   }
   if (buckets) {
