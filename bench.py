@@ -46,9 +46,12 @@ DESCRIPTIONS = {
                         "[128,1408,2816] + down [128,2816,704] bf16, N(0,0.02^2)"),
     "dense_5120": ("dense hidden-5120 Linears, quantize+dequantize of [5120,5120] + [17408,5120] + "
                    "[5120,17408] bf16, Student-t(5)*0.02"),
-    "kv_h256": ("KV cache K and V [1,4,32768,256] bf16 N(0,1), per-head H256, 8 centroids, 3-bit, "
-                "newest 128 tokens kept bf16; quantize+dequantize"),
+    "kv_h256": ("KV cache K and V [1,4,32768,256] bf16 N(0,1), per-head H256, 8 centroids, 3-bit "
+                "(4 centroids, 2-bit with --bits 2), newest 128 tokens kept bf16; quantize+dequantize"),
     "linear_64x256": "single Linear W[64,256] bf16 N(0,0.02^2), quantize+dequantize (launch-bound)",
+    "kv_h256_decode": ("streaming KV cache K and V [1,4,32768,256] bf16 N(0,1) with a 128-token bf16 window: "
+                       "one decode step appends one token to each of the 8 head caches (one launch), encoding "
+                       "the 8 tokens that leave the window (latency-bound)"),
 }
 
 
@@ -172,7 +175,7 @@ def weight_workload(torch, wq, dev, config, bits):
     }
 
 
-def kv_workload(torch, wq, dev, copies=2, n_residual=128):
+def kv_workload(torch, wq, dev, copies=2, n_residual=128, bits=3):
     """K and V of the cache held as one tensor [2 * batch, heads, tokens, 256]
     (K first), so one launch encodes (or decodes) both; two copies, and
     dequantize reads the copy that quantize did not just write."""
@@ -180,7 +183,7 @@ def kv_workload(torch, wq, dev, copies=2, n_residual=128):
     for c in range(copies):
         host = np.concatenate([synth.kv_cache("kv_h256", t, seed=synth.DEFAULT_SEED + c) for t in ("K", "V")], axis=0)
         kv = to_device(torch, dev, host)
-        p, n = wq.hlwq_kv_quantize(kv, n_residual=n_residual)
+        p, n = wq.hlwq_kv_quantize(kv, n_residual=n_residual, bits=bits)
         out = kv.clone()
         sets.append((kv, p, n, out))
     state = {"i": 0}
@@ -190,23 +193,98 @@ def kv_workload(torch, wq, dev, copies=2, n_residual=128):
 
     def quant():
         kv, p, n, _ = sets[state["i"] % copies]
-        wq.hlwq_kv_quantize(kv, n_residual=n_residual, packed=p, norms=n)
+        wq.hlwq_kv_quantize(kv, n_residual=n_residual, bits=bits, packed=p, norms=n)
 
     def dequant():
         _, p, n, out = sets[(state["i"] + 1) % copies]
-        wq.hlwq_kv_dequantize(p, n, out, n_residual=n_residual)
+        wq.hlwq_kv_dequantize(p, n, out, n_residual=n_residual, bits=bits)
         state["i"] += 1
 
     return {
         "quantize": quant,
         "dequantize": dequant,
         "weights": elems,
-        "bytes": elems * 2 + 2 * B * H * tq * (96 + 2),
+        "bytes": elems * 2 + 2 * B * H * tq * (32 * bits + 2),
         "kernels": ("hlwq_kv_quantize_kernel", "hlwq_kv_dequantize_kernel"),
         "launches": 1,
         "copies": copies,
         "keep": sets,
     }
+
+
+def decode_workload(torch, wq, dev, bits, steps_total, n_residual=128, pool=64):
+    """K and V caches (stacked, [2, 4, ...]) prefilled with 32768 tokens; each
+    step appends one token per head through hlwq_kv_append."""
+    host = np.concatenate([synth.kv_cache("kv_h256", t) for t in ("K", "V")], axis=0)
+    B, H, T, D = host.shape
+    kv = to_device(torch, dev, host)
+    cap = T - n_residual + steps_total + 1
+    packed = torch.empty((B, H, cap, 32 * bits), dtype=torch.uint8, device=dev)
+    norms = torch.empty((B, H, cap), dtype=torch.float16, device=dev)
+    p0, n0 = wq.hlwq_kv_quantize(kv, n_residual=n_residual, bits=bits)
+    packed[:, :, :T - n_residual] = p0
+    norms[:, :, :T - n_residual] = n0
+    window = torch.empty((B, H, n_residual, D), dtype=torch.bfloat16, device=dev)
+    for t in range(T - n_residual, T):
+        window[:, :, t % n_residual] = kv[:, :, t]
+    del kv, p0, n0
+    new = to_device(torch, dev, synth.random_bf16((pool, B, H, 1, D), seed=5, sigma=1.0))
+    state = {"tokens": T, "i": 0}
+
+    def step():
+        state["tokens"] = wq.hlwq_kv_append(new[state["i"] % pool], window, packed, norms, state["tokens"],
+                                            n_residual=n_residual, bits=bits)
+        state["i"] += 1
+
+    return step, B * H, B * H * (2 * D + 2 * D + 32 * bits + 2)
+
+
+def decode_main(args, bits):
+    import torch
+    import weight_quantization_amd as wq
+
+    wq.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    step, vectors, nbytes = decode_workload(torch, wq, dev, bits, args.warmup + args.steps)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        step()
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in range(args.steps)])
+    ms_per_step = wall * 1e3 / args.steps
+    result = {
+        "metric": "KV decode-step append: vectors encoded per second (latency-bound)",
+        "value": vectors / (ms_per_step * 1e-3),
+        "unit": "vectors/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": DESCRIPTIONS["kv_h256_decode"], "name": "kv_h256_decode", "bits": bits,
+                   "vectors_per_step": vectors},
+        "append": {"ms": round(float(ms.mean()), 4), "ms_median": round(float(np.median(ms)), 4),
+                   "ms_min": round(float(ms.min()), 4), "ms_max": round(float(ms.max()), 4)},
+        "roofline": {"bound": "hbm", "kernel": "hlwq_kv_append_kernel", "achieved":
+                     round(nbytes / (ms.mean() * 1e-3) / 1e9, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / (ms.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS, 6), "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": round(float(ms.mean()), 4),
+                     "note": "one launch moves a few KB: launch latency, not bandwidth, sets the time"},
+    }
+    print(json.dumps(result), flush=True)
 
 
 def _oracle_samples(config, bits, worker):
@@ -279,7 +357,7 @@ def main():
     # steady clocks; 1000 untimed steps is about 0.8 s on the default workload
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--config", default="qwen36_moe_bank", choices=sorted(DESCRIPTIONS))
-    ap.add_argument("--bits", type=int, default=None, choices=(5, 3))
+    ap.add_argument("--bits", type=int, default=None, choices=(5, 3, 2))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -287,9 +365,15 @@ def main():
               "exchange step, so one GPU's throughput is the per-GPU figure; use --gpus 1", file=sys.stderr)
         sys.exit(2)
     config = args.config
-    bits = args.bits if args.bits is not None else (3 if config == "kv_h256" else 5)
-    if config == "kv_h256" and bits != 3:
-        ap.error("the KV-cache path is 3-bit")
+    kv = config.startswith("kv_")
+    bits = args.bits if args.bits is not None else (3 if kv else 5)
+    if kv and bits not in (3, 2):
+        ap.error("the KV-cache path is 3- or 2-bit")
+    if not kv and bits not in (5, 3):
+        ap.error("weights are 5- or 3-bit")
+    if config == "kv_h256_decode":
+        decode_main(args, bits)
+        return
     print(f"[bench] timing the CPU oracle ({config}, Q{bits})", file=sys.stderr, flush=True)
 
     # the CPU oracle runs first, in forked processes, before this process
@@ -305,7 +389,7 @@ def main():
 
     print(f"[bench] generating {config}", file=sys.stderr, flush=True)
     if config == "kv_h256":
-        wl = kv_workload(torch, wq, dev)
+        wl = kv_workload(torch, wq, dev, bits=bits)
     else:
         wl = weight_workload(torch, wq, dev, config, bits)
     weights, bytes_dir, launches = wl["weights"], wl["bytes"], wl["launches"]

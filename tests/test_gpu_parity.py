@@ -362,6 +362,41 @@ def test_kv_h256_full(wq):
         assert np.array_equal(bf16_bits(out[bh:bh + 1, h:h + 1, t0:t0 + 512]), ref.kv_dequantize_c(op, on))
 
 
+@pytest.mark.parametrize("bits", [3, 2])
+def test_kv_decode_full(wq, bits):
+    # the benchmark's decode step: K and V caches [2, 4, 32768, 256] with a
+    # 128-token window, then single-token appends; the tokens that leave the
+    # window and the window itself are checked against the oracle
+    kv = np.concatenate([synth.kv_cache("kv_h256", t) for t in ("K", "V")], axis=0)
+    B, H, T, D = kv.shape
+    steps = 3
+    new = synth.random_bf16((B, H, steps, D), seed=5, sigma=1.0)
+    _say("kv decode full", bits)
+    dev = to_dev(kv)
+    cap = T - 128 + steps
+    packed = torch.empty((B, H, cap, 32 * bits), dtype=torch.uint8, device="cuda")
+    norms = torch.empty((B, H, cap), dtype=torch.float16, device="cuda")
+    p0, n0 = wq.hlwq_kv_quantize(dev, n_residual=128, bits=bits)
+    packed[:, :, :T - 128] = p0
+    norms[:, :, :T - 128] = n0
+    window = torch.empty((B, H, 128, D), dtype=torch.bfloat16, device="cuda")
+    for t in range(T - 128, T):
+        window[:, :, t % 128] = dev[:, :, t]
+    tokens = T
+    for i in range(steps):
+        tokens = wq.hlwq_kv_append(to_dev(new[:, :, i:i + 1]), window, packed, norms, tokens, bits=bits)
+    torch.cuda.synchronize()
+    left = kv[:, :, T - 128:T - 128 + steps]
+    codes, _, n16, _ = ref.quantize_vectors_c(ref.bf16_to_f32(left), bits)
+    assert np.array_equal(packed[:, :, T - 128:].cpu().numpy(), ref.pack_codes(codes, bits))
+    assert np.array_equal(f16_bits(norms[:, :, T - 128:]), n16.view(np.uint16))
+    assert np.array_equal(packed[:, :, :T - 128].cpu().numpy()[:, :, ::997], p0.cpu().numpy()[:, :, ::997])
+    w = bf16_bits(window)
+    for t in range(T - 128 + steps, T + steps):
+        want = kv[:, :, t] if t < T else new[:, :, t - T]
+        assert np.array_equal(w[:, :, t % 128], want), t
+
+
 # --------------------------------------------------------------------------
 # tolerances against the fp64 definition tier
 # --------------------------------------------------------------------------
