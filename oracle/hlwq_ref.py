@@ -355,3 +355,66 @@ def kv_stream_c(chunks, n_residual: int = 128, bits: int = 3, tables=None):
     out_n = np.stack(norms, axis=2) if norms else np.zeros((B, H, 0), np.float16)
     out_w = np.stack(list(window), axis=2) if window else np.zeros((B, H, 0, KV_DIM), np.uint16)
     return out_p, out_n, out_w
+
+
+# --------------------------------------------------------------------------
+# dequantize -> INT4 group-128 (the step after HLWQ in the pages' pipeline)
+# --------------------------------------------------------------------------
+
+INT4_LEVELS = 15  # codes 0..15
+
+
+def int4_quantize_c(w_bits: np.ndarray, group: int = BLOCK):
+    """Asymmetric 4-bit quantisation with one scale and zero point per group
+    of `group` consecutive columns of a row ("Qwopus3.6-27B-v2 · HLWQ Q5",
+    "Pipeline": dequantize per Linear to BF16, then a 4-bit weight-only
+    quantisation with group size 128 of the 128-aligned Linears; "Qwen3.5-9B —
+    HLWQ INT4", "Why HLWQ INT4 is Better": dequant -> INT4).
+
+    Readings (plain asymmetric min-max quantiser, fp32):
+      lo = min(0, min w), hi = max(0, max w) over the group (zero exactly
+      representable); scale = RN((hi - lo) / 15), 1 if that is 0;
+      inv = RN(1 / scale); zero point zp = clamp(rint(RN(-lo * inv)), 0, 15);
+      q = clamp(rint(RN(w * inv)) + zp, 0, 15), rint = round half to even.
+    Dequantised value: (q - zp) * scale.
+
+    w_bits: bf16 bits [rows, in], in % group == 0.  Returns q uint8 [rows, in]
+    (0..15), scales float32 [rows, in // group], zeros uint8 [rows, in // group].
+    """
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    rows, n_in = w_bits.shape
+    if n_in % group:
+        raise ValueError("in must be a multiple of the group size")
+    w = bf16_to_f32(w_bits).reshape(rows, n_in // group, group)
+    f = np.float32
+    lo = np.minimum(w.min(axis=-1), f(0))
+    hi = np.maximum(w.max(axis=-1), f(0))
+    scale = ((hi - lo) / f(INT4_LEVELS)).astype(f)
+    scale = np.where(scale == 0, f(1), scale).astype(f)
+    inv = (f(1) / scale).astype(f)
+    zp = np.clip(np.rint((-lo * inv).astype(f)), 0, INT4_LEVELS).astype(np.int64)
+    t = (w * inv[..., None]).astype(f)
+    q = np.clip(np.rint(t).astype(np.int64) + zp[..., None], 0, INT4_LEVELS)
+    return q.reshape(rows, n_in).astype(np.uint8), scale, zp.astype(np.uint8)
+
+
+def int4_pack(q: np.ndarray) -> np.ndarray:
+    """Two 4-bit codes per byte, element 2i in the low nibble: [..., n] -> [..., n / 2]."""
+    q = np.asarray(q, dtype=np.uint8)
+    return (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8)
+
+
+def int4_dequantize(q: np.ndarray, scales: np.ndarray, zeros: np.ndarray, group: int = BLOCK) -> np.ndarray:
+    """(q - zp) * scale, fp32 [rows, in]."""
+    rows, n_in = q.shape
+    qq = q.reshape(rows, n_in // group, group).astype(np.float32)
+    z = zeros.astype(np.float32)[..., None]
+    return ((qq - z) * scales[..., None]).astype(np.float32).reshape(rows, n_in)
+
+
+def dequantize_to_int4_c(packed: np.ndarray, n16: np.ndarray, n_in: int, bits: int, tables=None):
+    """HLWQ dequantize (tier C, bf16) followed by int4_quantize_c: returns packed
+    nibbles uint8 [rows, in / 2], scales float32 [rows, nb], zeros uint8 [rows, nb]."""
+    w = dequantize_c(packed, n16, n_in, bits, tables)
+    q, scales, zeros = int4_quantize_c(w)
+    return int4_pack(q), scales, zeros
