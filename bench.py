@@ -49,6 +49,9 @@ DESCRIPTIONS = {
     "kv_h256": ("KV cache K and V [1,4,32768,256] bf16 N(0,1), per-head H256, 8 centroids, 3-bit "
                 "(4 centroids, 2-bit with --bits 2), newest 128 tokens kept bf16; quantize+dequantize"),
     "linear_64x256": "single Linear W[64,256] bf16 N(0,0.02^2), quantize+dequantize (launch-bound)",
+    "dense_5120_int4": ("dense hidden-5120 Linears [5120,5120] + [17408,5120] + [5120,17408] bf16, "
+                        "Student-t(5)*0.02: HLWQ quantize, then dequantize straight to INT4 with a scale and "
+                        "zero point per 128-column group"),
     "kv_h256_decode": ("streaming KV cache K and V [1,4,32768,256] bf16 N(0,1) with a 128-token bf16 window: "
                        "one decode step appends one token to each of the 8 head caches (one launch), encoding "
                        "the 8 tokens that leave the window (latency-bound)"),
@@ -175,6 +178,51 @@ def weight_workload(torch, wq, dev, config, bits):
     }
 
 
+def int4_workload(torch, wq, dev, bits, config="dense_5120", copies=2):
+    """HLWQ quantize of the dense Linears (one grouped launch), then one
+    dequantize-to-INT4 launch per matrix; two rotating sets, as for the other
+    small working sets."""
+    tensors = list(synth.CONFIGS[config])
+    shapes = [tuple(synth.CONFIGS[config][t][1]) for t in tensors]
+    sets = []
+    for c in range(copies):
+        items, outs = [], []
+        for t, (out, n_in) in zip(tensors, shapes):
+            w = to_device(torch, dev, synth.weight(config, t, seed=synth.DEFAULT_SEED + c))
+            p, n = wq.hlwq_quantize(w, bits)
+            items.append((w, p, n))
+            outs.append((torch.empty((out, n_in // 2), dtype=torch.uint8, device=dev),
+                         torch.empty((out, n_in // 128), dtype=torch.float32, device=dev),
+                         torch.empty((out, n_in // 128), dtype=torch.uint8, device=dev)))
+        sets.append((items, outs))
+    state = {"i": 0}
+
+    def quant():
+        wq.hlwq_quantize_grouped(sets[state["i"] % copies][0], bits)
+
+    def to_int4():
+        items, outs = sets[(state["i"] + 1) % copies]
+        for (w, p, n), (q4, sc, z) in zip(items, outs):
+            wq.hlwq_dequantize_int4(p, n, w.shape[-1], bits, q4=q4, scales=sc, zeros=z)
+        state["i"] += 1
+
+    weights = sum(o * i for o, i in shapes)
+    blocks = weights // 128
+    return {
+        "quantize": quant,
+        "dequantize": to_int4,
+        "weights": weights,
+        "bytes": algorithmic_bytes([(1, o, i) for o, i in shapes], bits),
+        # codes + norm in; 64 B of nibbles + fp32 scale + u8 zero point out, per 128 weights
+        "bytes_d": blocks * (16 * bits + 2 + 64 + 4 + 1),
+        "kernels": (f"hlwq_quantize_kernel<{bits}>", f"hlwq_dequantize_int4_kernel<{bits}>"),
+        "launches": 1,
+        "launches_d": len(shapes),
+        "copies": copies,
+        "keep": sets,
+    }
+
+
 def kv_workload(torch, wq, dev, copies=2, n_residual=128, bits=3):
     """K and V of the cache held as one tensor [2 * batch, heads, tokens, 256]
     (K first), so one launch encodes (or decodes) both; two copies, and
@@ -293,13 +341,14 @@ def _oracle_samples(config, bits, worker):
     if config == "kv_h256":
         kv = synth.kv_cache("kv_h256", "K", tokens=1024 + 128)
         return [kv[:, worker % kv.shape[1]:][:, :1]]
+    source = "dense_5120" if config == "dense_5120_int4" else config
     samples = []
-    for t in synth.CONFIGS[config]:
-        tid, shape, dist, sigma, ofrac, omult = synth.CONFIGS[config][t]
+    for t in synth.CONFIGS[source]:
+        tid, shape, dist, sigma, ofrac, omult = synth.CONFIGS[source][t]
         if len(shape) == 3:
-            samples.append(synth.expert_matrix(config, t, worker % shape[0]))
+            samples.append(synth.expert_matrix(source, t, worker % shape[0]))
         else:
-            rng = synth.stream(synth.DEFAULT_SEED, synth.CONFIG_IDS[config], 90 + tid, worker)
+            rng = synth.stream(synth.DEFAULT_SEED, synth.CONFIG_IDS[source], 90 + tid, worker)
             samples.append(synth.draw(dist, rng, (min(shape[0], 256), shape[1]), sigma, ofrac, omult))
     return samples
 
@@ -318,6 +367,10 @@ def _oracle_worker(args):
                 p, n = ref.kv_quantize_c(w, n_residual=128)
                 ref.kv_dequantize_c(p, n)
                 done += p.shape[2] * 256
+            elif config == "dense_5120_int4":
+                packed, n16 = ref.quantize_c(w, bits)
+                ref.dequantize_to_int4_c(packed, n16, w.shape[1], bits)
+                done += w.size
             else:
                 packed, n16 = ref.quantize_c(w, bits)
                 ref.dequantize_c(packed, n16, w.shape[1], bits)
@@ -344,7 +397,8 @@ def cpu_baseline(config, bits, budget_s=10.0):
         "cores": cores,
         "kind": "oracle",
         "sample": f"{cores} processes x {budget_s:.0f} s, each on {what} of {config} (Q{bits} quantize+"
-                  f"dequantize, repeated): {done} weights in {wall:.1f} s; "
+                  f"{'dequantize to INT4' if config == 'dense_5120_int4' else 'dequantize'}, repeated): "
+                  f"{done} weights in {wall:.1f} s; "
                   f"{done / wall / cores:.3g} weights/s per core",
     }
 
@@ -390,9 +444,13 @@ def main():
     print(f"[bench] generating {config}", file=sys.stderr, flush=True)
     if config == "kv_h256":
         wl = kv_workload(torch, wq, dev, bits=bits)
+    elif config == "dense_5120_int4":
+        wl = int4_workload(torch, wq, dev, bits)
     else:
         wl = weight_workload(torch, wq, dev, config, bits)
     weights, bytes_dir, launches = wl["weights"], wl["bytes"], wl["launches"]
+    bytes_d = wl.get("bytes_d", bytes_dir)  # the second leg may move other bytes (INT4 output)
+    launches_d = wl.get("launches_d", launches)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -418,24 +476,25 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
 
     q_gbs = bytes_dir / (q_ms.mean() * 1e-3) / 1e9
-    d_gbs = bytes_dir / (d_ms.mean() * 1e-3) / 1e9
+    d_gbs = bytes_d / (d_ms.mean() * 1e-3) / 1e9
     dom = 0 if q_ms.mean() >= d_ms.mean() else 1
     dom_ms = max(q_ms.mean(), d_ms.mean())
-    achieved = bytes_dir / (dom_ms * 1e-3) / 1e9
+    dom_bytes, dom_launches = (bytes_dir, launches) if dom == 0 else (bytes_d, launches_d)
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = stored_traffic(config, bits)
     roofline = {
         "bound": "hbm",
-        "kernel": wl["kernels"][dom] + ("" if launches == 1 else f" ({launches} launches per step)"),
+        "kernel": wl["kernels"][dom] + ("" if dom_launches == 1 else f" ({dom_launches} launches per step)"),
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": (None if traffic is None else
                     traffic["quantize_bytes_per_launch" if dom == 0 else "dequantize_bytes_per_launch"]),
-        "algorithmic_bytes_per_launch": bytes_dir // launches,
-        "avg_launch_ms": round(dom_ms / launches, 4),
+        "algorithmic_bytes_per_launch": dom_bytes // dom_launches,
+        "avg_launch_ms": round(dom_ms / dom_launches, 4),
     }
-    step_gbs = 2 * bytes_dir / (ms_per_step * 1e-3) / 1e9
+    step_gbs = (bytes_dir + bytes_d) / (ms_per_step * 1e-3) / 1e9
     result = {
         "metric": METRIC,
         "value": weights / (ms_per_step * 1e-3),

@@ -117,6 +117,24 @@ int hlwq_quantize_grouped(const hlwq_mat_desc* mats, int n, int bits, void* hip_
 /* Inverse of hlwq_quantize_grouped over the same descriptors. */
 int hlwq_dequantize_grouped(const hlwq_mat_desc* mats, int n, int bits, void* hip_stream);
 
+/* Dequantize HLWQ codes straight to INT4 with one scale and zero point per
+ * group of 128 consecutive columns of a row, the step that follows in the
+ * pages' pipeline ("Qwopus3.6-27B-v2 · HLWQ Q5", "Pipeline": dequantize per
+ * Linear to BF16, then 4-bit weight-only quantisation with group size 128 of
+ * the 128-aligned Linears; "Qwen3.5-9B — HLWQ INT4", "Why HLWQ INT4 is
+ * Better").  The group is the HLWQ block; `in` must be a multiple of 128.  The
+ * bf16 values hlwq_dequantize would write are re-quantised in registers:
+ * per group, in fp32, lo = min(0, min w), hi = max(0, max w),
+ * scale = (hi - lo) / 15 (1 if that is 0), inv = 1 / scale,
+ * zp = clamp(rint(-lo * inv), 0, 15), q = clamp(rint(w * inv) + zp, 0, 15)
+ * (rint: nearest, ties to even); a weight dequantises to (q - zp) * scale.
+ * Outputs: q4_u8 [n_mats][out][in / 2] (element 2i in the low nibble of byte
+ * i), scales_f32 [n_mats][out][in / 128], zeros_u8 [n_mats][out][in / 128].
+ * bits 5 or 3, block 128.  packed and q4 16-byte aligned, norms 2-byte and
+ * scales 4-byte aligned. */
+int hlwq_dequantize_int4(const void* packed_u8, const void* norms_f16, int64_t n_mats, int64_t out, int64_t in,
+                         int block, int bits, void* q4_u8, void* scales_f32, void* zeros_u8, void* hip_stream);
+
 /* Quantize a KV cache [batch][heads][tokens][head_dim] (bf16) per head
  * vector: H256 rotation, 8 Lloyd-Max centroids, 3-bit codes ("Qwopus3.6-27B-v2
  * · HLWQ Q5", "Methodology notes", KV bullet), or with bits = 2 the 4-centroid

@@ -23,7 +23,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = wq.declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     raw = ctypes.CDLL(wq.binding.LIB_PATH)
     for name in names:
         assert hasattr(raw, name), name
@@ -177,3 +177,18 @@ def test_kv_append_argument_errors(lib):
     # nothing to append, or nobody to append to
     assert ap(None, 1, 4, 0, 500, None, 128, None, None, 0, 256, 3, None) == OK
     assert ap(None, 0, 4, 3, 500, None, 128, None, None, 0, 256, 3, None) == OK
+
+
+def test_dequantize_int4_argument_errors(lib):
+    A = 0x100000
+    d4 = lib.hlwq_dequantize_int4
+    # packed, norms, n_mats, out, in, block, bits, q4, scales, zeros, stream
+    assert d4(A, A, 1, 4, 256, 64, 5, A, A, A, None) == EBLOCK
+    assert d4(A, A, 1, 4, 256, 128, 4, A, A, A, None) == EBITS
+    assert d4(A, A, 1, 4, 200, 128, 5, A, A, A, None) == ESHAPE   # not 128-aligned
+    assert d4(A, A, -1, 4, 256, 128, 5, A, A, A, None) == ESHAPE
+    assert d4(A, A, 1, 4, 256, 128, 5, A, A, None, None) == ENULL
+    assert d4(A, A, 1, 4, 256, 128, 5, A + 8, A, A, None) == EALIGN
+    assert d4(A, A, 1, 4, 256, 128, 5, A, A + 2, A, None) == EALIGN
+    assert d4(A + 8, A, 1, 4, 256, 128, 5, A, A, A, None) == EALIGN
+    assert d4(None, None, 1, 0, 256, 128, 5, None, None, None, None) == OK

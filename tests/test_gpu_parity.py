@@ -278,6 +278,36 @@ def test_kv_cache_underflow_vectors(wq):
     assert np.array_equal(bf16_bits(out)[:, :, :72], ref.kv_dequantize_c(op, on))
 
 
+@pytest.mark.parametrize("bits", [5, 3])
+@pytest.mark.parametrize("shape", [(1, 7, 128), (1, 100, 256), (3, 40, 1024), (1, 3001, 384)])
+def test_dequantize_int4(wq, bits, shape):
+    E, rows, n_in = shape
+    wb = synth.random_bf16((E * rows, n_in), seed=rows + bits, dist="student_t5", sigma=0.02, outlier_frac=0.002,
+                           outlier_mult=20.0)
+    _say("dequantize -> int4", bits, shape)
+    packed, norms = wq.hlwq_quantize(to_dev(wb).view(E, rows, n_in), bits)
+    q4, scales, zeros = wq.hlwq_dequantize_int4(packed, norms, n_in, bits)
+    torch.cuda.synchronize()
+    op, on = ref.quantize_c(wb, bits)
+    p4, s4, z4 = ref.dequantize_to_int4_c(op, on, n_in, bits)
+    assert np.array_equal(q4.cpu().numpy().reshape(E * rows, -1), p4)
+    assert np.array_equal(scales.cpu().numpy().reshape(E * rows, -1).view(np.uint32), s4.view(np.uint32))
+    assert np.array_equal(zeros.cpu().numpy().reshape(E * rows, -1), z4)
+
+
+def test_dequantize_int4_special_blocks(wq):
+    w = _special_rows()
+    w[8, ::2] = 0x8000
+    packed, norms = wq.hlwq_quantize(to_dev(w), 5)
+    q4, scales, zeros = wq.hlwq_dequantize_int4(packed, norms, 256, 5)
+    torch.cuda.synchronize()
+    op, on = ref.quantize_c(w, 5)
+    p4, s4, z4 = ref.dequantize_to_int4_c(op, on, 256, 5)
+    assert np.array_equal(q4.cpu().numpy(), p4)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), s4.view(np.uint32))
+    assert np.array_equal(zeros.cpu().numpy(), z4)
+
+
 # --------------------------------------------------------------------------
 # full-size workloads, launched as the benchmark launches them; sampled outputs
 # --------------------------------------------------------------------------
@@ -339,6 +369,27 @@ def test_dense_5120_full_sampled_rows(wq, bits):
         assert np.array_equal(f16_bits(norms[idx]), on.view(np.uint16))
         assert np.array_equal(bf16_bits(out[idx]), ref.dequantize_c(op, on, wb.shape[1], bits))
         del w, packed, norms, out
+
+
+@pytest.mark.parametrize("bits", [5, 3])
+def test_dense_5120_int4_sampled_rows(wq, bits):
+    # the INT4 workload of the benchmark: every dense matrix, one
+    # dequantize-to-INT4 launch each, sampled rows checked
+    rng = np.random.default_rng(10 + bits)
+    for t in synth.CONFIGS["dense_5120"]:
+        wb = synth.weight("dense_5120", t)
+        _say("dense_5120 int4", t, wb.shape, "bits", bits)
+        packed, norms = wq.hlwq_quantize(to_dev(wb), bits)
+        q4, scales, zeros = wq.hlwq_dequantize_int4(packed, norms, wb.shape[1], bits)
+        torch.cuda.synchronize()
+        rows = np.sort(rng.choice(wb.shape[0], 64, replace=False))
+        idx = torch.from_numpy(rows).cuda()
+        op, on = ref.quantize_c(wb[rows], bits)
+        p4, s4, z4 = ref.dequantize_to_int4_c(op, on, wb.shape[1], bits)
+        assert np.array_equal(q4[idx].cpu().numpy(), p4)
+        assert np.array_equal(scales[idx].cpu().numpy().view(np.uint32), s4.view(np.uint32))
+        assert np.array_equal(zeros[idx].cpu().numpy(), z4)
+        del packed, norms, q4, scales, zeros
 
 
 def test_kv_h256_full(wq):

@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     hlwq_centroids,
     hlwq_dequantize,
     hlwq_dequantize_grouped,
+    hlwq_dequantize_int4,
     hlwq_kv_append,
     hlwq_kv_dequantize,
     hlwq_kv_quantize,

@@ -53,6 +53,7 @@ _SIGNATURES = {
     "hlwq_kv_quantize": (_int, [_vp, _i64, _i64, _i64, _int, _int, _i64, _vp, _vp, _vp]),
     "hlwq_kv_dequantize": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _i64, _vp, _vp]),
     "hlwq_kv_append": (_int, [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _int, _int, _vp]),
+    "hlwq_dequantize_int4": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp]),
     "hlwq_packed_bytes": (ctypes.c_size_t, [_i64, _i64, _int, _int]),
     "hlwq_norm_count": (ctypes.c_size_t, [_i64, _i64, _int]),
     "hlwq_search_table": (_int, [_int, ctypes.POINTER(ctypes.c_uint8), _int, ctypes.POINTER(ctypes.c_uint32),
@@ -213,6 +214,38 @@ def hlwq_dequantize(packed, norms, n_in: int, bits: int = 5, out=None, stream=No
                                         _stream_handle(stream))
     _check("hlwq_dequantize", st)
     return out
+
+
+def hlwq_dequantize_int4(packed, norms, n_in: int, bits: int = 5, q4=None, scales=None, zeros=None, stream=None):
+    """Dequantize to INT4 with a scale and zero point per 128-column group;
+    returns (q4 uint8 [.., out, in / 2], scales float32 [.., out, in / 128],
+    zeros uint8 [.., out, in / 128])."""
+    torch = _torch()
+    _need(packed, torch.uint8, "packed")
+    _need(norms, torch.float16, "norms")
+    if packed.dim() not in (3, 4) or packed.shape[-1] != 16 * bits:
+        raise ValueError("packed must be [.., out, nb, 16*bits]")
+    if n_in % BLOCK:
+        raise ValueError("in must be a multiple of 128")
+    lead = tuple(packed.shape[:-2])
+    nb = packed.shape[-2]
+    if nb != n_in // BLOCK or tuple(norms.shape) != lead + (nb,):
+        raise ValueError("packed / norms / in mismatch")
+    n_mats, rows = (1, lead[0]) if len(lead) == 1 else lead
+    dev = packed.device
+    q4 = torch.empty(lead + (n_in // 2,), dtype=torch.uint8, device=dev) if q4 is None else q4
+    scales = torch.empty(lead + (nb,), dtype=torch.float32, device=dev) if scales is None else scales
+    zeros = torch.empty(lead + (nb,), dtype=torch.uint8, device=dev) if zeros is None else zeros
+    _need(q4, torch.uint8, "q4")
+    _need(scales, torch.float32, "scales")
+    _need(zeros, torch.uint8, "zeros")
+    if tuple(q4.shape) != lead + (n_in // 2,) or tuple(scales.shape) != lead + (nb,) or \
+            tuple(zeros.shape) != lead + (nb,):
+        raise ValueError("q4 / scales / zeros shape mismatch")
+    st = load_library().hlwq_dequantize_int4(_ptr(packed), _ptr(norms), n_mats, rows, n_in, BLOCK, bits, _ptr(q4),
+                                             _ptr(scales), _ptr(zeros), _stream_handle(stream))
+    _check("hlwq_dequantize_int4", st)
+    return q4, scales, zeros
 
 
 def _descs(items):

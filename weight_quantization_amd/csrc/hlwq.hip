@@ -636,6 +636,111 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 }
 
 // ---------------------------------------------------------------------------
+// Dequantize straight to INT4 with one scale and zero point per 128-column
+// group (= one HLWQ block; `in` is a multiple of 128): the bf16 values the
+// dequantize kernel would write are formed in registers and re-quantised,
+// without the bf16 round trip through HBM.  Per group, in fp32:
+// lo = min(0, min w), hi = max(0, max w), scale = (hi - lo) / 15 (1 if 0),
+// inv = 1 / scale, zp = clamp(rint(-lo * inv), 0, 15),
+// q = clamp(rint(w * inv) + zp, 0, 15), two codes per byte, low nibble first.
+// ---------------------------------------------------------------------------
+
+struct Int4Args {
+  const uint8_t* packed;   // [nblocks][16 * bits]
+  const uint16_t* norms;   // [nblocks]
+  uint8_t* q4;             // [nblocks][64]
+  float* scales;           // [nblocks]
+  uint8_t* zeros;          // [nblocks]
+  uint32_t nblocks, total_batches;
+};
+
+constexpr float kRoundMagic = 12582912.0f;       // 1.5 * 2^23: x + it rounds x to an integer, ties to even
+constexpr int32_t kRoundMagicBits = 0x4B400000;  // its bit pattern
+
+template <int BITS>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_dequantize_int4_kernel(const Int4Args a) {
+  constexpr int kPairs = 8 << (2 * BITS);
+  constexpr uint32_t kIn = 16 * BITS;  // packed bytes per block
+  constexpr int kArea = 8192;          // per wave: the batch's codes in, then its nibbles out
+  __shared__ __attribute__((aligned(256))) uint8_t pairs[kPairs];
+  __shared__ __attribute__((aligned(256))) uint8_t areas[kWaves * kArea];
+  fill_pairs<BITS>(reinterpret_cast<float*>(pairs), (BITS == 5) ? c_cent5 : c_cent3);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* area = areas + wave * kArea;
+  SwzLane sl = swz_lane(lane);
+  uint32_t lane_a = 0;
+
+  for (uint32_t b = blockIdx.x * kWaves + wave; b < a.total_batches; b += gridDim.x * kWaves) {
+    refresh(sl, lane_a);
+    const uint32_t g0 = b * 64u;
+    const uint32_t left = a.nblocks - g0;
+    const uint32_t nvalid = left < 64u ? left : 64u;
+    // lanes past the end of the batch repeat the last block and store nothing
+    const uint32_t slot = static_cast<uint32_t>(lane) < nvalid ? static_cast<uint32_t>(lane) : nvalid - 1;
+    stage_in<BITS, false, 0>(a.packed + static_cast<size_t>(g0) * kIn, nvalid * kIn, area, lane, sl);
+    const float nscale = f16_value(a.norms[g0 + slot]) * 0x1p-7f;
+    wait_vmem();
+    uint32_t words[4 * BITS];
+#pragma unroll
+    for (int q = 0; q < BITS; ++q) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(area + kIn * slot + 16 * q);
+      words[4 * q] = v.x;
+      words[4 * q + 1] = v.y;
+      words[4 * q + 2] = v.z;
+      words[4 * q + 3] = v.w;
+    }
+    lds_handover();  // the area is refilled with output below
+
+    float v[kBlock];
+    decode_stage1<BITS, kBlock>(words, pairs, v);
+    fwht<kBlock, 2>(v);
+    // the bf16 values of the dequantised block, as fp32
+#pragma unroll
+    for (int j = 0; j < kBlock; j += 2) {
+      const uint32_t pk = pack_bf16x2(v[j] * nscale, v[j + 1] * nscale);
+      v[j] = bf16_lo(pk);
+      v[j + 1] = bf16_hi(pk);
+    }
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kBlock; ++j) {
+      lo = fminf(lo, v[j]);
+      hi = fmaxf(hi, v[j]);
+    }
+    float scale = (hi - lo) / 15.0f;
+    scale = (scale == 0.0f) ? 1.0f : scale;
+    const float inv = 1.0f / scale;
+    const int32_t zp = static_cast<int32_t>(__builtin_fminf(__builtin_fmaxf(__builtin_rintf(-lo * inv), 0.0f), 15.0f));
+    const int32_t bias = zp - kRoundMagicBits;
+    uint32_t nib[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      uint32_t acc = 0;
+#pragma unroll
+      for (int k = 7; k >= 0; --k) {
+        const int32_t r = static_cast<int32_t>(__float_as_uint(v[8 * m + k] * inv + kRoundMagic)) + bias;
+        const uint32_t q = static_cast<uint32_t>(r < 0 ? 0 : (r > 15 ? 15 : r));
+        acc = (acc << 4) | q;
+      }
+      nib[m] = acc;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 val = {nib[4 * q], nib[4 * q + 1], nib[4 * q + 2], nib[4 * q + 3]};
+      *reinterpret_cast<u32x4*>(area + 64 * lane + 16 * q) = val;
+    }
+    stage_out<4, false>(a.q4 + static_cast<size_t>(g0) * 64, nvalid * 64u, area, lane, sl);
+    if (static_cast<uint32_t>(lane) < nvalid) {
+      a.scales[g0 + lane] = scale;
+      a.zeros[g0 + lane] = static_cast<uint8_t>(zp);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // KV-cache kernels: a 256-wide head vector over two adjacent lanes; a wave
 // works on batches of 32 consecutive tokens of one head (16 KB of bf16).
 // ---------------------------------------------------------------------------
@@ -1034,6 +1139,33 @@ int run_kv(bool quant, const void* kv, void* packed, void* norms, int64_t batch,
   return launch_status();
 }
 
+int run_dequantize_int4(const void* packed, const void* norms, int64_t n_mats, int64_t out, int64_t in, int block,
+                        int bits, void* q4, void* scales, void* zeros, hipStream_t stream) {
+  if (block != kBlock) return HLWQ_ERR_BLOCK;
+  if (bits != 5 && bits != 3) return HLWQ_ERR_BITS;
+  if (n_mats < 0 || out < 0 || in < 0 || in % kBlock) return HLWQ_ERR_SHAPE;
+  int64_t rows, nblocks;
+  if (!mul_ok(n_mats, out, &rows) || !mul_ok(rows, in / kBlock, &nblocks)) return HLWQ_ERR_SHAPE;
+  if (nblocks == 0) return HLWQ_OK;
+  if (!packed || !norms || !q4 || !scales || !zeros) return HLWQ_ERR_NULL;
+  if (nblocks > 0x7fffffff - 64) return HLWQ_ERR_LIMIT;
+  if ((reinterpret_cast<uintptr_t>(packed) & 15u) || (reinterpret_cast<uintptr_t>(norms) & 1u) ||
+      (reinterpret_cast<uintptr_t>(q4) & 15u) || (reinterpret_cast<uintptr_t>(scales) & 3u))
+    return HLWQ_ERR_ALIGN;
+  Int4Args a;
+  a.packed = static_cast<const uint8_t*>(packed);
+  a.norms = static_cast<const uint16_t*>(norms);
+  a.q4 = static_cast<uint8_t*>(q4);
+  a.scales = static_cast<float*>(scales);
+  a.zeros = static_cast<uint8_t*>(zeros);
+  a.nblocks = static_cast<uint32_t>(nblocks);
+  a.total_batches = static_cast<uint32_t>(ceil_div(nblocks, 64));
+  const dim3 grid(persistent_grid(a.total_batches)), block_dim(kThreads);
+  if (bits == 5) hipLaunchKernelGGL(hlwq_dequantize_int4_kernel<5>, grid, block_dim, 0, stream, a);
+  else hipLaunchKernelGGL(hlwq_dequantize_int4_kernel<3>, grid, block_dim, 0, stream, a);
+  return launch_status();
+}
+
 int run_kv_append(const void* src, int64_t batch, int64_t heads, int64_t n_new, int64_t tokens, void* ring,
                   int64_t n_residual, void* packed, void* norms, int64_t capacity, int head_dim, int bits,
                   hipStream_t stream) {
@@ -1122,6 +1254,12 @@ int hlwq_kv_dequantize(const void* packed_u8, const void* norms_f16, int64_t bat
                        void* hip_stream) {
   return run_kv(false, kv_bf16_out, const_cast<void*>(packed_u8), const_cast<void*>(norms_f16), batch, heads,
                 tokens, head_dim, bits, n_residual, static_cast<hipStream_t>(hip_stream));
+}
+
+int hlwq_dequantize_int4(const void* packed_u8, const void* norms_f16, int64_t n_mats, int64_t out, int64_t in,
+                         int block, int bits, void* q4_u8, void* scales_f32, void* zeros_u8, void* hip_stream) {
+  return run_dequantize_int4(packed_u8, norms_f16, n_mats, out, in, block, bits, q4_u8, scales_f32, zeros_u8,
+                             static_cast<hipStream_t>(hip_stream));
 }
 
 int hlwq_kv_append(const void* new_kv_bf16, int64_t batch, int64_t heads, int64_t n_new, int64_t tokens,
