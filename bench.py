@@ -135,13 +135,14 @@ def to_device(torch, dev, bits_u16):
     return torch.from_numpy(np.ascontiguousarray(bits_u16).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-def weight_workload(torch, wq, dev, config, bits):
+def weight_workload(torch, wq, dev, config, bits, layout="packed"):
     tensors = list(synth.CONFIGS[config])
     shapes = []
     for t in tensors:
         shape = synth.CONFIGS[config][t][1]
         shapes.append((shape if len(shape) == 3 else (1, *shape)))
-    nbytes = algorithmic_bytes(shapes, bits)
+    field = 8 if layout == "codes8" else bits   # bits per stored code
+    nbytes = algorithmic_bytes(shapes, field)
     copies = 1 if nbytes >= _CACHE_SAFE_BYTES else 2
     sets = []
     for c in range(copies):
@@ -151,28 +152,42 @@ def weight_workload(torch, wq, dev, config, bits):
             w = to_device(torch, dev, synth.weight(config, t, seed=synth.DEFAULT_SEED + c))
             nb = -(-n_in // 128)
             lead = (E, out) if len(shape) == 3 else (out,)
-            p = torch.empty(lead + (nb, 16 * bits), dtype=torch.uint8, device=dev)
+            p = torch.empty(lead + (nb, 16 * field), dtype=torch.uint8, device=dev)
             n = torch.empty(lead + (nb,), dtype=torch.float16, device=dev)
             qitems.append((w, p, n))
             ditems.append((torch.empty_like(w), p, n))
-        wq.hlwq_quantize_grouped(qitems, bits)
         sets.append((qitems, ditems))
     state = {"i": 0}
 
-    def quant():
-        wq.hlwq_quantize_grouped(sets[state["i"] % copies][0], bits)
+    if layout == "codes8":   # one code per byte: one launch per tensor
+        def quant():
+            for w, p, n in sets[state["i"] % copies][0]:
+                wq.hlwq_quantize_codes8(w, bits, codes=p, norms=n)
 
-    def dequant():
-        wq.hlwq_dequantize_grouped(sets[(state["i"] + 1) % copies][1], bits)
-        state["i"] += 1
+        def dequant():
+            for o, p, n in sets[(state["i"] + 1) % copies][1]:
+                wq.hlwq_dequantize_codes8(p, n, o.shape[-1], bits, out=o)
+            state["i"] += 1
+    else:
+        def quant():
+            wq.hlwq_quantize_grouped(sets[state["i"] % copies][0], bits)
+
+        def dequant():
+            wq.hlwq_dequantize_grouped(sets[(state["i"] + 1) % copies][1], bits)
+            state["i"] += 1
+
+    for c in range(copies):
+        state["i"] = c
+        quant()
+    state["i"] = 0
 
     return {
         "quantize": quant,
         "dequantize": dequant,
         "weights": sum(E * o * i for E, o, i in shapes),
         "bytes": nbytes,
-        "kernels": (f"hlwq_quantize_kernel<{bits}>", f"hlwq_dequantize_kernel<{bits}>"),
-        "launches": 1,
+        "kernels": (f"hlwq_quantize_kernel<{bits}, {field}>", f"hlwq_dequantize_kernel<{bits}, {field}>"),
+        "launches": len(shapes) if layout == "codes8" else 1,
         "copies": copies,
         "keep": sets,
     }
@@ -413,6 +428,8 @@ def main():
     ap.add_argument("--config", default="qwen36_moe_bank", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--bits", type=int, default=None, choices=(5, 3, 2))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layout", default="packed", choices=("packed", "codes8"),
+                    help="weight codes packed (bits per code) or one code per byte")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the HLWQ path shards by expert, row or head with no "
@@ -447,7 +464,7 @@ def main():
     elif config == "dense_5120_int4":
         wl = int4_workload(torch, wq, dev, bits)
     else:
-        wl = weight_workload(torch, wq, dev, config, bits)
+        wl = weight_workload(torch, wq, dev, config, bits, layout=args.layout)
     weights, bytes_dir, launches = wl["weights"], wl["bytes"], wl["launches"]
     bytes_d = wl.get("bytes_d", bytes_dir)  # the second leg may move other bytes (INT4 output)
     launches_d = wl.get("launches_d", launches)
@@ -481,7 +498,7 @@ def main():
     dom_ms = max(q_ms.mean(), d_ms.mean())
     dom_bytes, dom_launches = (bytes_dir, launches) if dom == 0 else (bytes_d, launches_d)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = stored_traffic(config, bits)
+    traffic = stored_traffic(config, bits) if args.layout == "packed" else None
     roofline = {
         "bound": "hbm",
         "kernel": wl["kernels"][dom] + ("" if dom_launches == 1 else f" ({dom_launches} launches per step)"),
@@ -509,7 +526,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": DESCRIPTIONS[config], "name": config, "weights": weights, "bits": bits,
-                   "block": 256 if config == "kv_h256" else 128, "input_sets": wl["copies"]},
+                   "block": 256 if config == "kv_h256" else 128, "input_sets": wl["copies"],
+                   "layout": "packed" if config.startswith("kv_") else args.layout},
         "hbm_gbs": round(step_gbs, 1),
         "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "quantize": {"ms": round(float(q_ms.mean()), 4), "ms_median": round(float(np.median(q_ms)), 4),

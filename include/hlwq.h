@@ -107,6 +107,18 @@ int hlwq_dequantize(const void* packed_u8, const void* norms_f16, int64_t n_mats
                     int64_t out, int64_t in, int block, int bits,
                     void* w_bf16_out, void* hip_stream);
 
+/* The same quantisation with the codes stored one per byte instead of packed
+ * ("Gemma-4-26B-A4B-it-HLWQ-Q5", "Technical Details": int8 codes and fp16
+ * norms): codes_u8 [n_mats][out][nb][128], code j of a block in byte j (the
+ * zero-padded tail of a row's last block included).  bits 5 or 3. */
+int hlwq_quantize_codes8(const void* w_bf16, int64_t n_mats, int64_t out, int64_t in, int block, int bits,
+                         void* codes_u8, void* norms_f16, void* hip_stream);
+
+/* Inverse of hlwq_quantize_codes8.  Only the low `bits` bits of each code byte
+ * are read. */
+int hlwq_dequantize_codes8(const void* codes_u8, const void* norms_f16, int64_t n_mats, int64_t out, int64_t in,
+                           int block, int bits, void* w_bf16_out, void* hip_stream);
+
 /* Quantize several matrices (e.g. the gate_up and down banks of a MoE layer,
  * every expert of which is quantised independently: "Gemma-4-26B-A4B-it-HLWQ-Q5",
  * "Technical Details") in one launch.  `mats` is a host array of n

@@ -304,6 +304,21 @@ def dequantize_c(packed: np.ndarray, n16: np.ndarray, n_in: int, bits: int, tabl
     return f32_to_bf16_rne(w)
 
 
+def quantize_codes8_c(w_bits: np.ndarray, bits: int, tables=None):
+    """Tier C quantize with one code per byte ("Gemma-4-26B-A4B-it-HLWQ-Q5",
+    "Technical Details": int8 codes and fp16 norms): codes uint8
+    (rows, n_blocks, 128), fp16 norms (rows, n_blocks)."""
+    x, nb = blocks_from_rows(w_bits)
+    codes, _, n16, _ = quantize_vectors_c(x, bits, tables)
+    return codes.astype(np.uint8), n16
+
+
+def dequantize_codes8_c(codes: np.ndarray, n16: np.ndarray, n_in: int, bits: int, tables=None) -> np.ndarray:
+    """Inverse of quantize_codes8_c: -> bf16 bits (rows, in)."""
+    w = dequantize_vectors_c(np.asarray(codes, dtype=np.int64), n16, bits, tables)
+    return f32_to_bf16_rne(w.reshape(w.shape[0], -1)[:, :n_in])
+
+
 def kv_quantize_c(kv_bits: np.ndarray, n_residual: int = 128, bits: int = 3, tables=None):
     """Tier C KV-cache quantize of [B, H, T, 256] bf16.
 

@@ -23,7 +23,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = wq.declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     raw = ctypes.CDLL(wq.binding.LIB_PATH)
     for name in names:
         assert hasattr(raw, name), name
@@ -192,3 +192,16 @@ def test_dequantize_int4_argument_errors(lib):
     assert d4(A, A, 1, 4, 256, 128, 5, A, A + 2, A, None) == EALIGN
     assert d4(A + 8, A, 1, 4, 256, 128, 5, A, A, A, None) == EALIGN
     assert d4(None, None, 1, 0, 256, 128, 5, None, None, None, None) == OK
+
+
+def test_codes8_argument_errors(lib):
+    A = 0x100000
+    q, d = lib.hlwq_quantize_codes8, lib.hlwq_dequantize_codes8
+    assert q(None, 1, 4, 128, 128, 5, A, A, None) == ENULL
+    assert q(A, 1, 4, 128, 128, 4, A, A, None) == EBITS
+    assert q(A, 1, 4, 128, 64, 5, A, A, None) == EBLOCK
+    assert q(A, 1, 4, 128, 128, 5, A + 8, A, None) == EALIGN
+    assert q(None, 0, 4, 128, 128, 5, None, None, None) == OK
+    assert d(A, None, 1, 4, 128, 128, 5, A, None) == ENULL
+    assert d(A, A, 1, 4, 128, 128, 6, A, None) == EBITS
+    assert d(A, A, 1, -4, 128, 128, 5, A, None) == ESHAPE

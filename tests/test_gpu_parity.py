@@ -295,6 +295,26 @@ def test_dequantize_int4(wq, bits, shape):
     assert np.array_equal(zeros.cpu().numpy().reshape(E * rows, -1), z4)
 
 
+@pytest.mark.parametrize("bits", [5, 3])
+@pytest.mark.parametrize("shape", [(1, 64, 256), (1, 300, 704), (2, 33, 129), (1, 2001, 8)])
+def test_codes8(wq, bits, shape):
+    E, rows, n_in = shape
+    wb = synth.random_bf16((E * rows, n_in), seed=rows + n_in + bits, dist="student_t5")
+    _say("codes8", bits, shape)
+    codes, norms = wq.hlwq_quantize_codes8(to_dev(wb).view(E, rows, n_in), bits)
+    out = wq.hlwq_dequantize_codes8(codes, norms, n_in, bits)
+    # only the low `bits` bits of a code byte count
+    junk = codes | torch.tensor(0xE0 if bits == 5 else 0xF8, dtype=torch.uint8, device="cuda")
+    out2 = wq.hlwq_dequantize_codes8(junk, norms, n_in, bits)
+    torch.cuda.synchronize()
+    oc, on = ref.quantize_codes8_c(wb, bits)
+    assert np.array_equal(codes.cpu().numpy().reshape(oc.shape), oc)
+    assert np.array_equal(f16_bits(norms).reshape(on.shape), on.view(np.uint16))
+    want = ref.dequantize_codes8_c(oc, on, n_in, bits)
+    assert np.array_equal(bf16_bits(out).reshape(want.shape), want)
+    assert np.array_equal(bf16_bits(out2).reshape(want.shape), want)
+
+
 def test_dequantize_int4_special_blocks(wq):
     w = _special_rows()
     w[8, ::2] = 0x8000

@@ -245,3 +245,16 @@ def test_kv_q2_quality():
     x = ref.bf16_to_f32(kv[:, :, :172]).astype(np.float64)
     c = float(np.mean(np.sum(x * out, -1) / np.linalg.norm(x, axis=-1) / np.linalg.norm(out, axis=-1)))
     assert abs(c - math.sqrt(1 - 0.1175)) < 5e-3
+
+
+@pytest.mark.parametrize("bits", [5, 3])
+def test_codes8_layout_is_the_unpacked_codes(bits):
+    # one code per byte (int8 codes) holds exactly the codes the packed layout
+    # packs, and decodes to the same weights
+    w = synth.random_bf16((40, 300), seed=50 + bits)
+    codes, n16 = ref.quantize_codes8_c(w, bits)
+    packed, n16p = ref.quantize_c(w, bits)
+    assert codes.dtype == np.uint8 and codes.shape == (40, 3, 128)
+    assert np.array_equal(codes, ref.unpack_codes(packed, bits))
+    assert np.array_equal(n16.view(np.uint16), n16p.view(np.uint16))
+    assert np.array_equal(ref.dequantize_codes8_c(codes, n16, 300, bits), ref.dequantize_c(packed, n16p, 300, bits))

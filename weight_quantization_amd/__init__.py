@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     declared_functions,
     hlwq_centroids,
     hlwq_dequantize,
+    hlwq_dequantize_codes8,
     hlwq_dequantize_grouped,
     hlwq_dequantize_int4,
     hlwq_kv_append,
@@ -19,6 +20,7 @@ from .binding import (  # noqa: F401
     hlwq_norm_count,
     hlwq_packed_bytes,
     hlwq_quantize,
+    hlwq_quantize_codes8,
     hlwq_quantize_grouped,
     hlwq_search_table,
     hlwq_status_string,

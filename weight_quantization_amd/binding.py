@@ -54,6 +54,8 @@ _SIGNATURES = {
     "hlwq_kv_dequantize": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _i64, _vp, _vp]),
     "hlwq_kv_append": (_int, [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _int, _int, _vp]),
     "hlwq_dequantize_int4": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp]),
+    "hlwq_quantize_codes8": (_int, [_vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp]),
+    "hlwq_dequantize_codes8": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp]),
     "hlwq_packed_bytes": (ctypes.c_size_t, [_i64, _i64, _int, _int]),
     "hlwq_norm_count": (ctypes.c_size_t, [_i64, _i64, _int]),
     "hlwq_search_table": (_int, [_int, ctypes.POINTER(ctypes.c_uint8), _int, ctypes.POINTER(ctypes.c_uint32),
@@ -213,6 +215,48 @@ def hlwq_dequantize(packed, norms, n_in: int, bits: int = 5, out=None, stream=No
     st = load_library().hlwq_dequantize(_ptr(packed), _ptr(norms), n_mats, rows, n_in, BLOCK, bits, _ptr(out),
                                         _stream_handle(stream))
     _check("hlwq_dequantize", st)
+    return out
+
+
+def hlwq_quantize_codes8(w, bits: int = 5, codes=None, norms=None, stream=None):
+    """Quantize with one code per byte; returns (codes u8 [.., nb, 128], norms fp16 [.., nb])."""
+    torch = _torch()
+    _need(w, torch.bfloat16, "w")
+    if w.dim() not in (2, 3):
+        raise ValueError("w must be [out, in] or [n_mats, out, in]")
+    n_mats, out, n_in = (1, *w.shape) if w.dim() == 2 else tuple(w.shape)
+    pshape, nshape = packed_shape(tuple(w.shape), 8)
+    codes = torch.empty(pshape, dtype=torch.uint8, device=w.device) if codes is None else codes
+    norms = torch.empty(nshape, dtype=torch.float16, device=w.device) if norms is None else norms
+    _need(codes, torch.uint8, "codes")
+    _need(norms, torch.float16, "norms")
+    if tuple(codes.shape) != pshape or tuple(norms.shape) != nshape:
+        raise ValueError("codes / norms shape mismatch")
+    st = load_library().hlwq_quantize_codes8(_ptr(w), n_mats, out, n_in, BLOCK, bits, _ptr(codes), _ptr(norms),
+                                             _stream_handle(stream))
+    _check("hlwq_quantize_codes8", st)
+    return codes, norms
+
+
+def hlwq_dequantize_codes8(codes, norms, n_in: int, bits: int = 5, out=None, stream=None):
+    """Inverse of hlwq_quantize_codes8; returns bf16 [.., out, in]."""
+    torch = _torch()
+    _need(codes, torch.uint8, "codes")
+    _need(norms, torch.float16, "norms")
+    if codes.dim() not in (3, 4) or codes.shape[-1] != BLOCK:
+        raise ValueError("codes must be [.., out, nb, 128]")
+    lead = tuple(codes.shape[:-2])
+    nb = codes.shape[-2]
+    if nb != -(-n_in // BLOCK) or tuple(norms.shape) != lead + (nb,):
+        raise ValueError("codes / norms / in mismatch")
+    n_mats, rows = (1, lead[0]) if len(lead) == 1 else lead
+    out = torch.empty(lead + (n_in,), dtype=torch.bfloat16, device=codes.device) if out is None else out
+    _need(out, torch.bfloat16, "out")
+    if tuple(out.shape) != lead + (n_in,):
+        raise ValueError("out shape mismatch")
+    st = load_library().hlwq_dequantize_codes8(_ptr(codes), _ptr(norms), n_mats, rows, n_in, BLOCK, bits, _ptr(out),
+                                               _stream_handle(stream))
+    _check("hlwq_dequantize_codes8", st)
     return out
 
 

@@ -281,6 +281,23 @@ __device__ __forceinline__ void decode_stage1(const uint32_t (&w)[L * BITS / 32]
   }
 }
 
+// The same for codes stored one per byte (the low BITS bits of each byte):
+// the pair index of codes 2m and 2m+1 is assembled from two byte fields.
+template <int BITS, int L>
+__device__ __forceinline__ void decode_bytes_stage1(const uint32_t (&w)[L / 4], const uint8_t* __restrict__ pairs,
+                                                    float (&v)[L]) {
+#pragma unroll
+  for (int m = 0; m < L / 2; ++m) {
+    const uint32_t word = w[m >> 1];
+    const int sh = 16 * (m & 1);
+    const uint32_t lo = __builtin_amdgcn_ubfe(word, sh, BITS);
+    const uint32_t hi = __builtin_amdgcn_ubfe(word, sh + 8, BITS);
+    const float2 c = *reinterpret_cast<const float2*>(pairs + 8u * (lo | (hi << BITS)));
+    v[2 * m] = c.x;
+    v[2 * m + 1] = c.y;
+  }
+}
+
 // Fill the pair table of a K-centroid codebook (K * K entries of 8 bytes).
 template <int BITS>
 __device__ __forceinline__ void fill_pairs(float* pairs, const float* __restrict__ cent) {
@@ -517,7 +534,8 @@ __device__ __forceinline__ BatchPos batch_pos(const WeightGroup& g, int d, uint3
   return p;
 }
 
-template <int BITS>
+// FIELD: bits per stored code, BITS (packed) or 8 (one code per byte).
+template <int BITS, int FIELD>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_quantize_kernel(const WeightGroup g) {
   // one LDS array: the entry table at offset 0 (so its reads need no base
   // add), the bucket table, then the 256-byte aligned per-wave stages
@@ -536,7 +554,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   uint8_t* stage = stage_all + wave * kStage;
   SwzLane sl = swz_lane(lane);
   uint32_t lane_a = lds_addr(stage) + 256u * lane + 16u * (lane & 15);
-  constexpr uint32_t kOut = 16 * BITS;  // packed bytes per block
+  constexpr uint32_t kOut = 16 * FIELD;  // code bytes per block
 
   for (uint32_t b = blockIdx.x * kWaves + wave; b < g.total_batches; b += gridDim.x * kWaves) {
     refresh(sl, lane_a);
@@ -561,21 +579,21 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 
     const NormInfo ni = norm_info(sumsq_tree(x));
     fwht(x);
-    uint32_t words[4 * BITS];
-    encode<BITS, kBlock>(x, ni.r, lds, 256u, __uint_as_float(HLWQ_BUCKET_BIAS), words);
+    uint32_t words[4 * FIELD];
+    encode<FIELD, kBlock>(x, ni.r, lds, 256u, __uint_as_float(HLWQ_BUCKET_BIAS), words);
 
-    // packed output of the batch is contiguous: kOut bytes per block
+    // the codes of the batch are contiguous: kOut bytes per block
 #pragma unroll
-    for (int q = 0; q < BITS; ++q) {
+    for (int q = 0; q < FIELD; ++q) {
       const u32x4 v = {words[4 * q], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]};
       *reinterpret_cast<u32x4*>(stage + kOut * lane + 16 * q) = v;
     }
-    stage_out<BITS, false>(g.packed[d] + static_cast<size_t>(p.g0) * kOut, p.nvalid * kOut, stage, lane, sl);
+    stage_out<FIELD, false>(g.packed[d] + static_cast<size_t>(p.g0) * kOut, p.nvalid * kOut, stage, lane, sl);
     if (static_cast<uint32_t>(lane) < p.nvalid) g.norms[d][p.lb] = ni.n16;
   }
 }
 
-template <int BITS>
+template <int BITS, int FIELD>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_dequantize_kernel(const WeightGroup g) {
   // one LDS array: the centroid pair table at offset 0, then the per-wave stages
   constexpr int kPairs = 8 << (2 * BITS);
@@ -589,21 +607,21 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   uint8_t* stage = stage_all + wave * kStage;
   SwzLane sl = swz_lane(lane);
   uint32_t lane_a = lds_addr(stage) + 256u * lane + 16u * (lane & 15);
-  constexpr uint32_t kIn = 16 * BITS;  // packed bytes per block
+  constexpr uint32_t kIn = 16 * FIELD;  // code bytes per block
 
   for (uint32_t b = blockIdx.x * kWaves + wave; b < g.total_batches; b += gridDim.x * kWaves) {
     refresh(sl, lane_a);
     const int d = group_of(g, b);
     const BatchPos p = batch_pos(g, d, b, lane);
 
-    stage_in<BITS, false, 0>(g.packed[d] + static_cast<size_t>(p.g0) * kIn, p.nvalid * kIn, stage, lane, sl);
+    stage_in<FIELD, false, 0>(g.packed[d] + static_cast<size_t>(p.g0) * kIn, p.nvalid * kIn, stage, lane, sl);
     const float scale = f16_value(g.norms[d][p.lb]) * 0x1p-7f;
     wait_vmem();
     // lanes past the end of the batch read (and later write) the last block
     const uint32_t slot = p.lb - p.g0;
-    uint32_t words[4 * BITS];
+    uint32_t words[4 * FIELD];
 #pragma unroll
-    for (int q = 0; q < BITS; ++q) {
+    for (int q = 0; q < FIELD; ++q) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(stage + kIn * slot + 16 * q);
       words[4 * q] = v.x;
       words[4 * q + 1] = v.y;
@@ -612,7 +630,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     }
 
     float v[kBlock];
-    decode_stage1<BITS, kBlock>(words, lds, v);
+    if constexpr (FIELD == BITS) decode_stage1<BITS, kBlock>(words, lds, v);
+    else decode_bytes_stage1<BITS, kBlock>(words, lds, v);
     fwht<kBlock, 2>(v);
     uint32_t pk[kBlock / 2];
 #pragma unroll
@@ -1037,8 +1056,9 @@ uint32_t persistent_grid(uint32_t batches) {
   return static_cast<uint32_t>(want < cap ? want : cap);
 }
 
+// field: bits per stored code (bits for packed codes, 8 for one code per byte)
 template <bool QUANT>
-int run_weight_group(const hlwq_mat_desc* mats, int n, int bits, hipStream_t stream) {
+int run_weight_group(const hlwq_mat_desc* mats, int n, int bits, int field, hipStream_t stream) {
   if (n < 0) return HLWQ_ERR_SHAPE;
   if (n > 0 && !mats) return HLWQ_ERR_NULL;
   if (bits != 5 && bits != 3) return HLWQ_ERR_BITS;
@@ -1074,12 +1094,23 @@ int run_weight_group(const hlwq_mat_desc* mats, int n, int bits, hipStream_t str
     g.batch_start[g.n] = static_cast<uint32_t>(batches);
     g.total_batches = static_cast<uint32_t>(batches);
     const dim3 grid(persistent_grid(g.total_batches)), block(kThreads);
+    const bool bytes = field == 8;
     if (QUANT) {
-      if (bits == 5) hipLaunchKernelGGL(hlwq_quantize_kernel<5>, grid, block, 0, stream, g);
-      else hipLaunchKernelGGL(hlwq_quantize_kernel<3>, grid, block, 0, stream, g);
+      if (bits == 5) {
+        if (bytes) hipLaunchKernelGGL((hlwq_quantize_kernel<5, 8>), grid, block, 0, stream, g);
+        else hipLaunchKernelGGL((hlwq_quantize_kernel<5, 5>), grid, block, 0, stream, g);
+      } else {
+        if (bytes) hipLaunchKernelGGL((hlwq_quantize_kernel<3, 8>), grid, block, 0, stream, g);
+        else hipLaunchKernelGGL((hlwq_quantize_kernel<3, 3>), grid, block, 0, stream, g);
+      }
     } else {
-      if (bits == 5) hipLaunchKernelGGL(hlwq_dequantize_kernel<5>, grid, block, 0, stream, g);
-      else hipLaunchKernelGGL(hlwq_dequantize_kernel<3>, grid, block, 0, stream, g);
+      if (bits == 5) {
+        if (bytes) hipLaunchKernelGGL((hlwq_dequantize_kernel<5, 8>), grid, block, 0, stream, g);
+        else hipLaunchKernelGGL((hlwq_dequantize_kernel<5, 5>), grid, block, 0, stream, g);
+      } else {
+        if (bytes) hipLaunchKernelGGL((hlwq_dequantize_kernel<3, 8>), grid, block, 0, stream, g);
+        else hipLaunchKernelGGL((hlwq_dequantize_kernel<3, 3>), grid, block, 0, stream, g);
+      }
     }
     const int st = launch_status();
     if (st != HLWQ_OK) return st;
@@ -1224,7 +1255,7 @@ int hlwq_quantize(const void* w_bf16, int64_t n_mats, int64_t out, int64_t in, i
   hlwq_mat_desc m;
   const int st = make_single(w_bf16, packed_u8, norms_f16, n_mats, out, in, block, bits, &m);
   if (st != HLWQ_OK) return st;
-  return run_weight_group<true>(&m, 1, bits, static_cast<hipStream_t>(hip_stream));
+  return run_weight_group<true>(&m, 1, bits, bits, static_cast<hipStream_t>(hip_stream));
 }
 
 int hlwq_dequantize(const void* packed_u8, const void* norms_f16, int64_t n_mats, int64_t out, int64_t in,
@@ -1232,15 +1263,31 @@ int hlwq_dequantize(const void* packed_u8, const void* norms_f16, int64_t n_mats
   hlwq_mat_desc m;
   const int st = make_single(w_bf16_out, packed_u8, norms_f16, n_mats, out, in, block, bits, &m);
   if (st != HLWQ_OK) return st;
-  return run_weight_group<false>(&m, 1, bits, static_cast<hipStream_t>(hip_stream));
+  return run_weight_group<false>(&m, 1, bits, bits, static_cast<hipStream_t>(hip_stream));
 }
 
 int hlwq_quantize_grouped(const hlwq_mat_desc* mats, int n, int bits, void* hip_stream) {
-  return run_weight_group<true>(mats, n, bits, static_cast<hipStream_t>(hip_stream));
+  return run_weight_group<true>(mats, n, bits, bits, static_cast<hipStream_t>(hip_stream));
 }
 
 int hlwq_dequantize_grouped(const hlwq_mat_desc* mats, int n, int bits, void* hip_stream) {
-  return run_weight_group<false>(mats, n, bits, static_cast<hipStream_t>(hip_stream));
+  return run_weight_group<false>(mats, n, bits, bits, static_cast<hipStream_t>(hip_stream));
+}
+
+int hlwq_quantize_codes8(const void* w_bf16, int64_t n_mats, int64_t out, int64_t in, int block, int bits,
+                         void* codes_u8, void* norms_f16, void* hip_stream) {
+  hlwq_mat_desc m;
+  const int st = make_single(w_bf16, codes_u8, norms_f16, n_mats, out, in, block, bits, &m);
+  if (st != HLWQ_OK) return st;
+  return run_weight_group<true>(&m, 1, bits, 8, static_cast<hipStream_t>(hip_stream));
+}
+
+int hlwq_dequantize_codes8(const void* codes_u8, const void* norms_f16, int64_t n_mats, int64_t out, int64_t in,
+                           int block, int bits, void* w_bf16_out, void* hip_stream) {
+  hlwq_mat_desc m;
+  const int st = make_single(w_bf16_out, codes_u8, norms_f16, n_mats, out, in, block, bits, &m);
+  if (st != HLWQ_OK) return st;
+  return run_weight_group<false>(&m, 1, bits, 8, static_cast<hipStream_t>(hip_stream));
 }
 
 int hlwq_kv_quantize(const void* kv_bf16, int64_t batch, int64_t heads, int64_t tokens, int head_dim, int bits,
