@@ -52,20 +52,24 @@ DESCRIPTIONS = {
     "dense_5120_int4": ("dense hidden-5120 Linears [5120,5120] + [17408,5120] + [5120,17408] bf16, "
                         "Student-t(5)*0.02: HLWQ quantize, then dequantize straight to INT4 with a scale and "
                         "zero point per 128-column group"),
+    "qwen36_moe_bank_tq3": ("Qwen3.6-35B-A3B-shaped MoE layer (the model of the TQ3 checkpoint), TQ3 "
+                            "quantize+dequantize of gate_up [256,1024,2048] + down [256,2048,512] bf16, "
+                            "N(0,0.02^2) with 0.1% x20 outliers: random-sign H128 (seed 42), 8 Lloyd-Max "
+                            "centroids, 3-bit codes, fp32 shape-gain norms"),
     "kv_h256_decode": ("streaming KV cache K and V [1,4,32768,256] bf16 N(0,1) with a 128-token bf16 window: "
                        "one decode step appends one token to each of the 8 head caches (one launch), encoding "
                        "the 8 tokens that leave the window (latency-bound)"),
 }
 
 
-def algorithmic_bytes(shapes, bits=5):
-    """bf16 weights + packed codes + fp16 norms moved by one direction."""
+def algorithmic_bytes(shapes, bits=5, norm_bytes=2):
+    """bf16 weights + packed codes + norms (fp16, or TQ3's fp32) moved by one direction."""
     w = p = n = 0
     for E, out, n_in in shapes:
         nb = -(-n_in // 128)
         w += E * out * n_in * 2
         p += E * out * nb * 16 * bits
-        n += E * out * nb * 2
+        n += E * out * nb * norm_bytes
     return w + p + n
 
 
@@ -136,13 +140,16 @@ def to_device(torch, dev, bits_u16):
 
 
 def weight_workload(torch, wq, dev, config, bits, layout="packed"):
+    tq3 = config.endswith("_tq3")
+    if tq3:
+        config = config[:-len("_tq3")]
     tensors = list(synth.CONFIGS[config])
     shapes = []
     for t in tensors:
         shape = synth.CONFIGS[config][t][1]
         shapes.append((shape if len(shape) == 3 else (1, *shape)))
     field = 8 if layout == "codes8" else bits   # bits per stored code
-    nbytes = algorithmic_bytes(shapes, field)
+    nbytes = algorithmic_bytes(shapes, field, 4 if tq3 else 2)
     copies = 1 if nbytes >= _CACHE_SAFE_BYTES else 2
     sets = []
     for c in range(copies):
@@ -153,7 +160,7 @@ def weight_workload(torch, wq, dev, config, bits, layout="packed"):
             nb = -(-n_in // 128)
             lead = (E, out) if len(shape) == 3 else (out,)
             p = torch.empty(lead + (nb, 16 * field), dtype=torch.uint8, device=dev)
-            n = torch.empty(lead + (nb,), dtype=torch.float16, device=dev)
+            n = torch.empty(lead + (nb,), dtype=torch.float32 if tq3 else torch.float16, device=dev)
             qitems.append((w, p, n))
             ditems.append((torch.empty_like(w), p, n))
         sets.append((qitems, ditems))
@@ -167,6 +174,13 @@ def weight_workload(torch, wq, dev, config, bits, layout="packed"):
         def dequant():
             for o, p, n in sets[(state["i"] + 1) % copies][1]:
                 wq.hlwq_dequantize_codes8(p, n, o.shape[-1], bits, out=o)
+            state["i"] += 1
+    elif tq3:
+        def quant():
+            wq.hlwq_tq3_quantize_grouped(sets[state["i"] % copies][0], 42)
+
+        def dequant():
+            wq.hlwq_tq3_dequantize_grouped(sets[(state["i"] + 1) % copies][1], 42)
             state["i"] += 1
     else:
         def quant():
@@ -186,7 +200,8 @@ def weight_workload(torch, wq, dev, config, bits, layout="packed"):
         "dequantize": dequant,
         "weights": sum(E * o * i for E, o, i in shapes),
         "bytes": nbytes,
-        "kernels": (f"hlwq_quantize_kernel<{bits}, {field}>", f"hlwq_dequantize_kernel<{bits}, {field}>"),
+        "kernels": ((f"hlwq_quantize_kernel<3, 3, true>", f"hlwq_dequantize_kernel<3, 3, true>") if tq3 else
+                    (f"hlwq_quantize_kernel<{bits}, {field}>", f"hlwq_dequantize_kernel<{bits}, {field}>")),
         "launches": len(shapes) if layout == "codes8" else 1,
         "copies": copies,
         "keep": sets,
@@ -356,7 +371,7 @@ def _oracle_samples(config, bits, worker):
     if config == "kv_h256":
         kv = synth.kv_cache("kv_h256", "K", tokens=1024 + 128)
         return [kv[:, worker % kv.shape[1]:][:, :1]]
-    source = "dense_5120" if config == "dense_5120_int4" else config
+    source = {"dense_5120_int4": "dense_5120", "qwen36_moe_bank_tq3": "qwen36_moe_bank"}.get(config, config)
     samples = []
     for t in synth.CONFIGS[source]:
         tid, shape, dist, sigma, ofrac, omult = synth.CONFIGS[source][t]
@@ -372,7 +387,9 @@ def _oracle_worker(args):
     config, bits, worker, budget_s = args
     from oracle import hlwq_ref as ref
     from oracle import lloyd_max
+    from oracle import tq3_ref
     lloyd_max.table(bits)  # the codebook is computed once, outside the timing
+    tq3_ref.sign_vectors(42)
     samples = _oracle_samples(config, bits, worker)
     done = 0
     t0 = time.perf_counter()
@@ -382,6 +399,10 @@ def _oracle_worker(args):
                 p, n = ref.kv_quantize_c(w, n_residual=128)
                 ref.kv_dequantize_c(p, n)
                 done += p.shape[2] * 256
+            elif config == "qwen36_moe_bank_tq3":
+                packed, g = tq3_ref.quantize_c(w, 42)
+                tq3_ref.dequantize_c(packed, g, w.shape[1], 42)
+                done += w.size
             elif config == "dense_5120_int4":
                 packed, n16 = ref.quantize_c(w, bits)
                 ref.dequantize_to_int4_c(packed, n16, w.shape[1], bits)
@@ -411,7 +432,8 @@ def cpu_baseline(config, bits, budget_s=10.0):
         "unit": "weights/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"{cores} processes x {budget_s:.0f} s, each on {what} of {config} (Q{bits} quantize+"
+        "sample": f"{cores} processes x {budget_s:.0f} s, each on {what} of {config} "
+                  f"({'TQ3' if config.endswith('_tq3') else f'Q{bits}'} quantize+"
                   f"{'dequantize to INT4' if config == 'dense_5120_int4' else 'dequantize'}, repeated): "
                   f"{done} weights in {wall:.1f} s; "
                   f"{done / wall / cores:.3g} weights/s per core",
@@ -437,7 +459,9 @@ def main():
         sys.exit(2)
     config = args.config
     kv = config.startswith("kv_")
-    bits = args.bits if args.bits is not None else (3 if kv else 5)
+    bits = args.bits if args.bits is not None else (3 if kv or config.endswith("_tq3") else 5)
+    if config.endswith("_tq3") and (bits != 3 or args.layout != "packed"):
+        ap.error("TQ3 is 3-bit with packed codes")
     if kv and bits not in (3, 2):
         ap.error("the KV-cache path is 3- or 2-bit")
     if not kv and bits not in (5, 3):

@@ -119,6 +119,48 @@ int hlwq_quantize_codes8(const void* w_bf16, int64_t n_mats, int64_t out, int64_
 int hlwq_dequantize_codes8(const void* codes_u8, const void* norms_f16, int64_t n_mats, int64_t out, int64_t in,
                            int block, int bits, void* w_bf16_out, void* hip_stream);
 
+/* TQ3, the scalar case of HIGGS ("Qwen3.6-35B-A3B-TQ3-native", section "What
+ * TQ3 actually does"; stored tensors and quantizer state in section "Files").
+ * Per group of 128 consecutive values of a row (the last group zero-padded):
+ *   rotate  : y = D2 H D1 x * (1 / n), n the group's norm, H the unnormalised
+ *             Walsh-Hadamard butterflies, D1 and D2 diagonal +-1 sign vectors
+ *             drawn from `seed` (see hlwq_tq3_signs);
+ *   code    : nearest of the 8 Lloyd-Max centroids for N(0, 1), as hlwq Q3;
+ *   norm    : the shape-gain n / (rho / sqrt(128)), rho the norm of the
+ *             selected centroids, stored as fp32;
+ *   inverse : bf16 of D1 H D2 c[codes] * (norm / 128).
+ * Fixed fp32 operation order, shared with the HLWQ kernels where the steps
+ * coincide: the norm tree, 1 / n and the butterflies as above, y's sign flip
+ * after the rounding of z * (1 / n); rho^2 is the adjacent-pair tree over
+ * RN(c^2) (level 0 RN(e0 + e1)), rho and n / t correctly rounded,
+ * t = RN(rho * RN(1 / sqrt(128))); the inverse multiplies by RN(norm * 2^-7)
+ * and flips D1's signs after rounding.  Layouts: packed u8
+ * [n_mats][out][ng][48] in the 3-bit packing above (ng = ceil(in / 128)),
+ * norms fp32 [n_mats][out][ng] (4-byte aligned).  `group` must be 128.  The
+ * page records the seed (42) but not its generator, so codes are bit-identical
+ * to this library's oracle, not to checkpoints made by other tools. */
+
+/* The two sign vectors for `seed`: SplitMix64 (Steele, Lea & Flood, OOPSLA
+ * 2014) output i, i = 0 .. 255, has its top bit set when entry i of D1
+ * (i < 128) or entry i - 128 of D2 is -1.  Writes 8 words to the host array
+ * sign_words: bit i % 32 of word i / 32 for entry i of D1 (words 0-3) and of
+ * D2 (words 4-7).  Host only; returns HLWQ_OK or HLWQ_ERR_NULL. */
+int hlwq_tq3_signs(uint64_t seed, uint32_t* sign_words);
+
+/* TQ3-quantize W [n_mats][out][in] (bf16): packed u8 [n_mats][out][ng][48] and
+ * fp32 shape-gain norms [n_mats][out][ng]. */
+int hlwq_tq3_quantize(const void* w_bf16, int64_t n_mats, int64_t out, int64_t in, int group, uint64_t seed,
+                      void* packed_u8, void* norms_f32, void* hip_stream);
+
+/* Inverse of hlwq_tq3_quantize; writes only the `in` real columns of each row. */
+int hlwq_tq3_dequantize(const void* packed_u8, const void* norms_f32, int64_t n_mats, int64_t out, int64_t in,
+                        int group, uint64_t seed, void* w_bf16_out, void* hip_stream);
+
+/* Grouped forms, as hlwq_quantize_grouped / hlwq_dequantize_grouped: the
+ * descriptors' `norms` point to fp32 norms. */
+int hlwq_tq3_quantize_grouped(const hlwq_mat_desc* mats, int n, uint64_t seed, void* hip_stream);
+int hlwq_tq3_dequantize_grouped(const hlwq_mat_desc* mats, int n, uint64_t seed, void* hip_stream);
+
 /* Quantize several matrices (e.g. the gate_up and down banks of a MoE layer,
  * every expert of which is quantised independently: "Gemma-4-26B-A4B-it-HLWQ-Q5",
  * "Technical Details") in one launch.  `mats` is a host array of n

@@ -12,6 +12,7 @@ import pytest
 import weight_quantization_amd as wq
 from oracle import hlwq_ref as ref
 from oracle import lloyd_max as lm
+from oracle import tq3_ref as tq
 
 OK, ENULL, ESHAPE, EBITS, EBLOCK, EDEV, EALIGN, ELIMIT = 0, -1, -2, -3, -4, -5, -6, -7
 
@@ -23,7 +24,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = wq.declared_functions()
-    assert len(names) == 15
+    assert len(names) == 20
     raw = ctypes.CDLL(wq.binding.LIB_PATH)
     for name in names:
         assert hasattr(raw, name), name
@@ -205,3 +206,32 @@ def test_codes8_argument_errors(lib):
     assert d(A, None, 1, 4, 128, 128, 5, A, None) == ENULL
     assert d(A, A, 1, 4, 128, 128, 6, A, None) == EBITS
     assert d(A, A, 1, -4, 128, 128, 5, A, None) == ESHAPE
+
+
+@pytest.mark.parametrize("seed", [0, 1, 42, 1234567, 2 ** 64 - 1])
+def test_tq3_signs_match_oracle(seed):
+    # two independent SplitMix64 implementations (C in the library, Python in
+    # the oracle), both written from the generator's published definition
+    d1, d2 = wq.hlwq_tq3_signs(seed)
+    o1, o2 = tq.sign_vectors(seed)
+    assert np.array_equal(d1, o1) and np.array_equal(d2, o2)
+
+
+def test_tq3_argument_errors(lib):
+    A = 0x100000
+    q, d = lib.hlwq_tq3_quantize, lib.hlwq_tq3_dequantize
+    assert lib.hlwq_tq3_signs(42, None) == ENULL
+    assert q(None, 1, 4, 128, 128, 42, A, A, None) == ENULL
+    assert q(A, 1, 4, 128, 64, 42, A, A, None) == EBLOCK
+    assert q(A, 1, 4, 128, 128, 42, A + 8, A, None) == EALIGN
+    assert q(A, 1, 4, 128, 128, 42, A, A + 2, None) == EALIGN  # fp32 norms: 4-byte aligned
+    assert q(A, 1, -4, 128, 128, 42, A, A, None) == ESHAPE
+    assert q(None, 0, 4, 128, 128, 42, None, None, None) == OK
+    assert d(A, None, 1, 4, 128, 128, 42, A, None) == ENULL
+    assert d(A, A + 2, 1, 4, 128, 128, 42, A, None) == EALIGN
+    assert d(A, A, 1, 4, 200, 256, 42, A, None) == EBLOCK
+    descs = (wq.MatDesc * 1)()
+    descs[0] = wq.MatDesc(A, A, A + 2, 4, 128)
+    assert lib.hlwq_tq3_quantize_grouped(descs, 1, 42, None) == EALIGN
+    assert lib.hlwq_tq3_dequantize_grouped(None, 1, 42, None) == ENULL
+    assert lib.hlwq_tq3_quantize_grouped(descs, -1, 42, None) == ESHAPE

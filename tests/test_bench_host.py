@@ -15,6 +15,8 @@ def test_algorithmic_bytes_of_the_bank_workloads():
     assert bench.algorithmic_bytes([(128, 1408, 2816), (128, 2816, 704)], 5) == 2_024_996_864
     assert bench.algorithmic_bytes([(1, 64, 256)], 5) == 43_264
     assert bench.algorithmic_bytes([(1, 5120, 5120)], 3) == 52_428_800 + 10_240_000
+    # TQ3: 48 B of codes and a 4-byte fp32 norm per group of 128
+    assert bench.algorithmic_bytes([(256, 1024, 2048), (256, 2048, 512)], 3, 4) == 1_937_768_448
 
 
 def test_more_than_one_gpu_is_refused_with_a_message():

@@ -499,3 +499,126 @@ def test_definition_tier_tolerances(wq, bits):
     far = np.abs(ghat - dd_bf16) > 1e-3 * n_d[..., None]
     _say(f"bits={bits}: dequant beyond 1e-3*n of the rounded fp64 inverse: {int(far.sum())} ({far.mean():.2e})")
     assert far.mean() < 1e-5
+
+
+# --------------------------------------------------------------------------
+# TQ3 ("Qwen3.6-35B-A3B-TQ3-native", section "What TQ3 actually does")
+# --------------------------------------------------------------------------
+
+def f32_bits(t) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int32).numpy().view(np.uint32)
+
+
+def check_tq3(wq, w_bits: np.ndarray, seed: int, label: str, w=None, out=None):
+    rows, n_in = w_bits.shape
+    _say("tq3", label, "rows", rows, "in", n_in, "seed", seed)
+    w = to_dev(w_bits) if w is None else w
+    packed, norms = wq.hlwq_tq3_quantize(w, seed)
+    out = wq.hlwq_tq3_dequantize(packed, norms, n_in, seed, out=out)
+    torch.cuda.synchronize()
+    from oracle import tq3_ref as tq
+    op, on = tq.quantize_c(w_bits, seed)
+    assert np.array_equal(f32_bits(norms), on.view(np.uint32)), f"{label}: fp32 norms differ"
+    assert np.array_equal(packed.cpu().numpy(), op), f"{label}: packed codes differ"
+    assert np.array_equal(bf16_bits(out), tq.dequantize_c(op, on, n_in, seed)), f"{label}: bf16 differs"
+    return out
+
+
+@pytest.mark.parametrize("seed", [42, 7])
+@pytest.mark.parametrize("n_in", [1, 8, 127, 128, 129, 200, 704, 1000])
+def test_tq3_shapes_and_tails(wq, seed, n_in):
+    w = synth.random_bf16((67, n_in), seed=n_in + 1, key=5)
+    check_tq3(wq, w, seed, f"tails-{n_in}")
+
+
+def test_tq3_many_tiles(wq):
+    w = synth.random_bf16((3001, 384), seed=15, outlier_frac=0.001, outlier_mult=20.0)
+    check_tq3(wq, w, 42, "tiles-outliers")
+    w = synth.random_bf16((257, 1536), seed=16, dist="student_t5")
+    check_tq3(wq, w, 2 ** 64 - 1, "tiles-t5")
+
+
+def test_tq3_special_blocks(wq):
+    w = _special_rows()
+    w[8, ::2] = 0x8000
+    check_tq3(wq, w, 42, "special")
+
+
+def test_tq3_unaligned_rows(wq):
+    for n_in in (129, 704):
+        w_bits = synth.random_bf16((41, n_in), seed=n_in, key=6)
+        base = torch.zeros(41 * n_in + 1, dtype=torch.bfloat16, device="cuda")
+        base[1:] = to_dev(w_bits).reshape(-1)
+        outbuf = torch.zeros(41 * n_in + 1, dtype=torch.bfloat16, device="cuda")
+        check_tq3(wq, w_bits, 42, f"unaligned-{n_in}", w=base[1:].view(41, n_in), out=outbuf[1:].view(41, n_in))
+        assert bf16_bits(outbuf[:1])[0] == 0
+
+
+def test_tq3_dequantize_arbitrary_codes(wq):
+    # every code value at every position, norms over a wide range (not only
+    # what the quantizer produces)
+    from oracle import tq3_ref as tq
+    rng = np.random.default_rng(21)
+    rows, n_in = 300, 512
+    packed = rng.integers(0, 256, (rows, 4, 48), dtype=np.uint8)
+    norms = (np.exp(rng.uniform(-20, 20, (rows, 4))) * rng.choice([1.0, 0.0], (rows, 4), p=[0.95, 0.05]))
+    norms = norms.astype(np.float32)
+    _say("tq3 arbitrary codes")
+    out = wq.hlwq_tq3_dequantize(torch.from_numpy(packed).cuda(), torch.from_numpy(norms).cuda(), n_in, 42)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(out), tq.dequantize_c(packed, norms, n_in, 42))
+
+
+def test_tq3_grouped_launch(wq):
+    from oracle import tq3_ref as tq
+    rng = np.random.default_rng(22)
+    items, host = [], []
+    for i in range(18):
+        rows = int(rng.integers(1, 200))
+        n_in = int(rng.choice([64, 128, 200, 512, 704]))
+        wb = synth.random_bf16((rows, n_in), seed=300 + i)
+        nb = -(-n_in // 128)
+        items.append((to_dev(wb), torch.empty((rows, nb, 48), dtype=torch.uint8, device="cuda"),
+                      torch.empty((rows, nb), dtype=torch.float32, device="cuda")))
+        host.append(wb)
+    _say("tq3 grouped, 18 matrices")
+    wq.hlwq_tq3_quantize_grouped(items, 42)
+    outs = [(torch.empty_like(w), p, n) for (w, p, n) in items]
+    wq.hlwq_tq3_dequantize_grouped(outs, 42)
+    torch.cuda.synchronize()
+    for (w, p, n), (o, _, _), wb in zip(items, outs, host):
+        op, on = tq.quantize_c(wb, 42)
+        assert np.array_equal(p.cpu().numpy(), op)
+        assert np.array_equal(f32_bits(n), on.view(np.uint32))
+        assert np.array_equal(bf16_bits(o), tq.dequantize_c(op, on, wb.shape[1], 42))
+
+
+def test_tq3_qwen36_moe_bank_full(wq):
+    # the page's TQ3 checkpoint is of this model: the full MoE layer in one
+    # grouped launch, sampled experts against the oracle
+    from oracle import tq3_ref as tq
+    config = "qwen36_moe_bank"
+    tensors = list(synth.CONFIGS[config])
+    host = {t: synth.weight(config, t) for t in tensors}
+    items = []
+    for t in tensors:
+        E, rows, n_in = host[t].shape
+        nb = -(-n_in // 128)
+        items.append((to_dev(host[t]), torch.empty((E, rows, nb, 48), dtype=torch.uint8, device="cuda"),
+                      torch.empty((E, rows, nb), dtype=torch.float32, device="cuda")))
+    _say("tq3", config, "generated")
+    wq.hlwq_tq3_quantize_grouped(items, 42)
+    outs = [(torch.empty_like(w), p, n) for (w, p, n) in items]
+    wq.hlwq_tq3_dequantize_grouped(outs, 42)
+    torch.cuda.synchronize()
+    _say("tq3", config, "gpu done")
+    for t, (w, p, n), (o, _, _) in zip(tensors, items, outs):
+        for e in (0, 101, 255):
+            wb = host[t][e]
+            op, on = tq.quantize_c(wb, 42)
+            assert np.array_equal(p[e].cpu().numpy(), op), (t, e)
+            assert np.array_equal(f32_bits(n[e]), on.view(np.uint32)), (t, e)
+            assert np.array_equal(bf16_bits(o[e]), tq.dequantize_c(op, on, wb.shape[1], 42)), (t, e)
+        assert torch.isfinite(n).all() and (n > 0).all()
+    del items, outs
+    torch.cuda.empty_cache()

@@ -24,5 +24,10 @@ from .binding import (  # noqa: F401
     hlwq_quantize_grouped,
     hlwq_search_table,
     hlwq_status_string,
+    hlwq_tq3_dequantize,
+    hlwq_tq3_dequantize_grouped,
+    hlwq_tq3_quantize,
+    hlwq_tq3_quantize_grouped,
+    hlwq_tq3_signs,
     load_library,
 )

@@ -56,6 +56,11 @@ _SIGNATURES = {
     "hlwq_dequantize_int4": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp]),
     "hlwq_quantize_codes8": (_int, [_vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp]),
     "hlwq_dequantize_codes8": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp]),
+    "hlwq_tq3_signs": (_int, [ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint32)]),
+    "hlwq_tq3_quantize": (_int, [_vp, _i64, _i64, _i64, _int, ctypes.c_uint64, _vp, _vp, _vp]),
+    "hlwq_tq3_dequantize": (_int, [_vp, _vp, _i64, _i64, _i64, _int, ctypes.c_uint64, _vp, _vp]),
+    "hlwq_tq3_quantize_grouped": (_int, [ctypes.POINTER(MatDesc), _int, ctypes.c_uint64, _vp]),
+    "hlwq_tq3_dequantize_grouped": (_int, [ctypes.POINTER(MatDesc), _int, ctypes.c_uint64, _vp]),
     "hlwq_packed_bytes": (ctypes.c_size_t, [_i64, _i64, _int, _int]),
     "hlwq_norm_count": (ctypes.c_size_t, [_i64, _i64, _int]),
     "hlwq_search_table": (_int, [_int, ctypes.POINTER(ctypes.c_uint8), _int, ctypes.POINTER(ctypes.c_uint32),
@@ -118,6 +123,19 @@ def hlwq_centroids(bits: int):
     t = (ctypes.c_float * max(K - 1, 1))()
     _check("hlwq_centroids", load_library().hlwq_centroids(bits, c, t))
     return np.frombuffer(c, dtype=np.float32).copy(), np.frombuffer(t, dtype=np.float32)[:K - 1].copy()
+
+
+TQ3_SEED = 42  # the quantizer state's seed (bits 3, group 128)
+
+
+def hlwq_tq3_signs(seed: int = TQ3_SEED):
+    """TQ3's sign vectors for `seed` as two int8 arrays of +-1 (D1, D2), from the library."""
+    import numpy as np
+    words = (ctypes.c_uint32 * 8)()
+    _check("hlwq_tq3_signs", load_library().hlwq_tq3_signs(seed & (2 ** 64 - 1), words))
+    bits = np.array([(words[i >> 5] >> (i & 31)) & 1 for i in range(256)], dtype=np.int8)
+    s = (1 - 2 * bits).astype(np.int8)
+    return s[:128].copy(), s[128:].copy()
 
 
 def hlwq_search_table(kind: int):
@@ -260,6 +278,48 @@ def hlwq_dequantize_codes8(codes, norms, n_in: int, bits: int = 5, out=None, str
     return out
 
 
+def hlwq_tq3_quantize(w, seed: int = TQ3_SEED, packed=None, norms=None, stream=None):
+    """TQ3-quantize a bf16 [out, in] or [n_mats, out, in] tensor; returns (packed u8 [.., ng, 48], norms fp32 [.., ng])."""
+    torch = _torch()
+    _need(w, torch.bfloat16, "w")
+    if w.dim() not in (2, 3):
+        raise ValueError("w must be [out, in] or [n_mats, out, in]")
+    n_mats, out, n_in = (1, *w.shape) if w.dim() == 2 else tuple(w.shape)
+    pshape, nshape = packed_shape(tuple(w.shape), 3)
+    packed = torch.empty(pshape, dtype=torch.uint8, device=w.device) if packed is None else packed
+    norms = torch.empty(nshape, dtype=torch.float32, device=w.device) if norms is None else norms
+    _need(packed, torch.uint8, "packed")
+    _need(norms, torch.float32, "norms")
+    if tuple(packed.shape) != pshape or tuple(norms.shape) != nshape:
+        raise ValueError("packed / norms shape mismatch")
+    st = load_library().hlwq_tq3_quantize(_ptr(w), n_mats, out, n_in, BLOCK, seed & (2 ** 64 - 1), _ptr(packed),
+                                          _ptr(norms), _stream_handle(stream))
+    _check("hlwq_tq3_quantize", st)
+    return packed, norms
+
+
+def hlwq_tq3_dequantize(packed, norms, n_in: int, seed: int = TQ3_SEED, out=None, stream=None):
+    """Inverse of hlwq_tq3_quantize; returns bf16 [.., out, in]."""
+    torch = _torch()
+    _need(packed, torch.uint8, "packed")
+    _need(norms, torch.float32, "norms")
+    if packed.dim() not in (3, 4) or packed.shape[-1] != 48:
+        raise ValueError("packed must be [.., out, ng, 48]")
+    lead = tuple(packed.shape[:-2])
+    nb = packed.shape[-2]
+    if nb != -(-n_in // BLOCK) or tuple(norms.shape) != lead + (nb,):
+        raise ValueError("packed / norms / in mismatch")
+    n_mats, rows = (1, lead[0]) if len(lead) == 1 else lead
+    out = torch.empty(lead + (n_in,), dtype=torch.bfloat16, device=packed.device) if out is None else out
+    _need(out, torch.bfloat16, "out")
+    if tuple(out.shape) != lead + (n_in,):
+        raise ValueError("out shape mismatch")
+    st = load_library().hlwq_tq3_dequantize(_ptr(packed), _ptr(norms), n_mats, rows, n_in, BLOCK,
+                                            seed & (2 ** 64 - 1), _ptr(out), _stream_handle(stream))
+    _check("hlwq_tq3_dequantize", st)
+    return out
+
+
 def hlwq_dequantize_int4(packed, norms, n_in: int, bits: int = 5, q4=None, scales=None, zeros=None, stream=None):
     """Dequantize to INT4 with a scale and zero point per 128-column group;
     returns (q4 uint8 [.., out, in / 2], scales float32 [.., out, in / 128],
@@ -329,6 +389,33 @@ def hlwq_dequantize_grouped(items, bits: int = 5, stream=None):
     arr = _descs(items)
     st = load_library().hlwq_dequantize_grouped(arr, len(items), bits, _stream_handle(stream))
     _check("hlwq_dequantize_grouped", st)
+
+
+def _check_tq3_items(items):
+    torch = _torch()
+    for w, p, n in items:
+        _need(w, torch.bfloat16, "w")
+        _need(p, torch.uint8, "packed")
+        _need(n, torch.float32, "norms")
+        ps, ns = packed_shape(tuple(w.shape), 3)
+        if tuple(p.shape) != ps or tuple(n.shape) != ns:
+            raise ValueError("packed / norms shape mismatch")
+
+
+def hlwq_tq3_quantize_grouped(items, seed: int = TQ3_SEED, stream=None):
+    """items: list of (w bf16, packed u8, norms fp32) triples, all preallocated."""
+    _check_tq3_items(items)
+    st = load_library().hlwq_tq3_quantize_grouped(_descs(items), len(items), seed & (2 ** 64 - 1),
+                                                  _stream_handle(stream))
+    _check("hlwq_tq3_quantize_grouped", st)
+
+
+def hlwq_tq3_dequantize_grouped(items, seed: int = TQ3_SEED, stream=None):
+    """items: list of (w_out bf16, packed u8, norms fp32) triples, all preallocated."""
+    _check_tq3_items(items)
+    st = load_library().hlwq_tq3_dequantize_grouped(_descs(items), len(items), seed & (2 ** 64 - 1),
+                                                    _stream_handle(stream))
+    _check("hlwq_tq3_dequantize_grouped", st)
 
 
 def hlwq_kv_quantize(kv, n_residual: int = 128, bits: int = 3, packed=None, norms=None, stream=None):

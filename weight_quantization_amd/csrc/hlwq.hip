@@ -199,15 +199,41 @@ __device__ __forceinline__ void fwht(float (&v)[L]) {
 
 // Norm, fp16 norm and reciprocal of a block whose squared norm is s.
 struct NormInfo {
-  float r;
+  float n, r;
   uint16_t n16;
 };
 __device__ __forceinline__ NormInfo norm_info(float s) {
   const float n = sqrtf(s);
   NormInfo ni;
+  ni.n = n;
   ni.n16 = f16_bits(n);
   ni.r = (n >= FLT_MIN) ? 1.0f / n : 0.0f;
   return ni;
+}
+
+// A 128-bit string of TQ3 signs, bit i of word i / 32 for entry i (set: the
+// entry is -1).  Uniform across the grid, so it and every mask below live in
+// scalar registers.
+struct SignBits {
+  uint32_t w[4];
+};
+// the sign bit (0 or 1 << 31) that negates entry i
+__device__ __forceinline__ uint32_t sign_bit(const SignBits& s, int i) {
+  return (s.w[i >> 5] << (31 - (i & 31))) & 0x80000000u;
+}
+// The same bits, opaque to the compiler from here on: called once per batch,
+// it keeps every mask derived from them inside the batch loop (a few scalar
+// operations each) instead of hoisted out of it, where 256 live masks would
+// overflow the scalar register file.
+__device__ __forceinline__ SignBits per_batch(SignBits s) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) asm volatile("" : "+s"(s.w[i]));
+  return s;
+}
+// the xor mask that negates bf16 entries 2m (low half) and 2m + 1 (high half)
+// of a packed pair
+__device__ __forceinline__ uint32_t pair_sign_mask(const SignBits& s, int m) {
+  return (sign_bit(s, 2 * m) >> 16) | sign_bit(s, 2 * m + 1);
 }
 
 // Code of one rotated value y = z * r.  u = fma(y, 2^-146, bias) is a
@@ -217,9 +243,10 @@ __device__ __forceinline__ NormInfo norm_info(float s) {
 // entry table at LDS offset 0, and the code is base + (y > threshold).  The
 // table generator proves this equals the number of fp32 thresholds strictly
 // below y for every reachable y.
-__device__ __forceinline__ uint32_t code_of(float z, float r, const uint8_t* __restrict__ lds, uint32_t bucket,
-                                            float bias) {
-  const float y = z * r;
+// `flip` (0 or the sign bit) negates y first: TQ3's output sign vector.
+__device__ __forceinline__ uint32_t code_of(float z, float r, uint32_t flip, const uint8_t* __restrict__ lds,
+                                            uint32_t bucket, float bias) {
+  const float y = __uint_as_float(__float_as_uint(z * r) ^ flip);
   const uint32_t k = __float_as_uint(__builtin_fmaf(y, HLWQ_SEARCH_SCALE, bias));
   const uint32_t e = lds[bucket + k];
   const uint2 v = *reinterpret_cast<const uint2*>(lds + e);
@@ -231,10 +258,13 @@ __device__ __forceinline__ uint32_t code_of(float z, float r, const uint8_t* __r
 // bit string.  Words are built top-down by Horner steps acc = (acc << BITS) +
 // code; a code that straddles two words is computed once, finishes the upper
 // word's bottom bits and starts the lower word.
-template <int BITS, int L>
+// With FLIP, the y of value j is negated where bit j of the 128-bit string
+// `s2` is set (TQ3's D2).
+template <int BITS, int L, bool FLIP = false>
 __device__ __forceinline__ void encode(const float (&z)[L], float r, const uint8_t* __restrict__ lds, uint32_t bucket,
-                                       float bias, uint32_t (&w)[L * BITS / 32]) {
+                                       float bias, uint32_t (&w)[L * BITS / 32], const SignBits& s2 = SignBits{}) {
   constexpr int W = L * BITS / 32;
+  auto code = [&](int j) { return code_of(z[j], r, FLIP ? sign_bit(s2, j) : 0u, lds, bucket, bias); };
   uint32_t carry = 0;  // straddling code shared with the word below
 #pragma unroll
   for (int wi = W - 1; wi >= 0; --wi) {
@@ -242,11 +272,11 @@ __device__ __forceinline__ void encode(const float (&z)[L], float r, const uint8
     const int jlo = (32 * wi + BITS - 1) / BITS;        // first code starting in this word
     const int off = BITS * jlo - 32 * wi;               // its bit position (0 .. BITS-1)
     const bool top_shared = (BITS * jhi + BITS > 32 * (wi + 1)) && (jhi < L);
-    uint32_t acc = top_shared ? carry : code_of(z[jhi], r, lds, bucket, bias);
+    uint32_t acc = top_shared ? carry : code(jhi);
 #pragma unroll
-    for (int j = jhi - 1; j >= jlo; --j) acc = (acc << BITS) + code_of(z[j], r, lds, bucket, bias);
+    for (int j = jhi - 1; j >= jlo; --j) acc = (acc << BITS) + code(j);
     if (off > 0) {
-      const uint32_t c = code_of(z[jlo - 1], r, lds, bucket, bias);
+      const uint32_t c = code(jlo - 1);
       acc = (acc << off) + (c >> (BITS - off));
       carry = c;
     }
@@ -262,20 +292,25 @@ __device__ __forceinline__ void encode(const float (&z)[L], float r, const uint8
 // {c[a] + c[b], c[a] - c[b]}, computed with the same fp32 operations.  One
 // 8-byte read serves two values; its byte offset 8 i comes out of the packed
 // words with one shift or funnel shift and one mask.
+template <int BITS, int SH, int W>
+__device__ __forceinline__ uint32_t pair_offset(const uint32_t (&w)[W], int m) {
+  constexpr uint32_t kMask = ((1u << (2 * BITS)) - 1u) << SH;
+  const int p = 2 * BITS * m;  // bit position of pair m
+  const int lo = p & 31, wi = p >> 5;
+  uint32_t off;
+  if (lo + 2 * BITS <= 32)
+    off = (lo >= SH) ? (w[wi] >> (lo - SH)) : (w[wi] << (SH - lo));
+  else
+    off = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], lo - SH);
+  return off & kMask;
+}
+
 template <int BITS, int L>
 __device__ __forceinline__ void decode_stage1(const uint32_t (&w)[L * BITS / 32], const uint8_t* __restrict__ pairs,
                                               float (&v)[L]) {
-  constexpr uint32_t kMask = ((1u << (2 * BITS)) - 1u) << 3;
 #pragma unroll
   for (int m = 0; m < L / 2; ++m) {
-    const int p = 2 * BITS * m;  // bit position of pair m
-    const int lo = p & 31, wi = p >> 5;
-    uint32_t off;
-    if (lo + 2 * BITS <= 32)
-      off = (lo >= 3) ? (w[wi] >> (lo - 3)) : (w[wi] << (3 - lo));
-    else
-      off = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], lo - 3);
-    const float2 c = *reinterpret_cast<const float2*>(pairs + (off & kMask));
+    const float2 c = *reinterpret_cast<const float2*>(pairs + pair_offset<BITS, 3>(w, m));
     v[2 * m] = c.x;
     v[2 * m + 1] = c.y;
   }
@@ -295,6 +330,31 @@ __device__ __forceinline__ void decode_bytes_stage1(const uint32_t (&w)[L / 4], 
     const float2 c = *reinterpret_cast<const float2*>(pairs + 8u * (lo | (hi << BITS)));
     v[2 * m] = c.x;
     v[2 * m + 1] = c.y;
+  }
+}
+
+// Squared norm of the centroids a block's codes select, by the adjacent-pair
+// tree: level 0 is read from a table (LDS offset `sq`) holding, for every
+// 2*BITS-bit pair index i with a = i mod 2^BITS and b = i >> BITS,
+// RN(RN(c[a]^2) + RN(c[b]^2)); every further level adds neighbouring sums.
+template <int BITS, int L>
+__device__ __forceinline__ float recon_sumsq(const uint32_t (&w)[L * BITS / 32], const uint8_t* __restrict__ sq) {
+  float s[L / 2];
+#pragma unroll
+  for (int m = 0; m < L / 2; ++m) s[m] = *reinterpret_cast<const float*>(sq + pair_offset<BITS, 2>(w, m));
+#pragma unroll
+  for (int k = L / 4; k >= 1; k >>= 1)
+#pragma unroll
+    for (int i = 0; i < k; ++i) s[i] = s[2 * i] + s[2 * i + 1];
+  return s[0];
+}
+
+template <int BITS>
+__device__ __forceinline__ void fill_pair_squares(float* sq, const float* __restrict__ cent) {
+  constexpr int K = 1 << BITS;
+  for (int i = threadIdx.x; i < K * K; i += kThreads) {
+    const float a = cent[i & (K - 1)], b = cent[i >> BITS];
+    sq[i] = a * a + b * b;
   }
 }
 
@@ -491,6 +551,16 @@ __device__ __forceinline__ void stage_out_full(__amdgpu_buffer_rsrc_t dst, uint3
 // columns).  The workgroups loop over batches (persistent grid).
 // ---------------------------------------------------------------------------
 
+// TQ3's quantizer state for a launch: the two sign vectors, and D2 once more
+// as a mask over a block's 384-bit string of 3-bit codes (0b111 on every code
+// whose D2 entry is -1).  Negating a centroid is the same as mirroring its
+// code, c[7 - k] = -c[k] exactly (the codebook is symmetric), and 7 - k = k ^ 7,
+// so the dequantizer applies D2 with one xor per code word.
+struct TqSigns {
+  SignBits d1, d2;
+  uint32_t flip2[12];
+};
+
 struct WeightGroup {
   int32_t n;                           // matrices in this launch
   uint32_t total_batches;              // sum of batches over the matrices
@@ -502,7 +572,8 @@ struct WeightGroup {
   int64_t in[kMaxGroup];               // columns
   uint16_t* w[kMaxGroup];
   uint8_t* packed[kMaxGroup];
-  uint16_t* norms[kMaxGroup];
+  void* norms[kMaxGroup];              // fp16 (HLWQ) or fp32 (TQ3)
+  TqSigns tq;                          // TQ3 launches only
 };
 
 // matrix owning batch b (uniform across the wave)
@@ -535,11 +606,18 @@ __device__ __forceinline__ BatchPos batch_pos(const WeightGroup& g, int d, uint3
 }
 
 // FIELD: bits per stored code, BITS (packed) or 8 (one code per byte).
-template <int BITS, int FIELD>
+// TQ: TQ3 ("Qwen3.6-35B-A3B-TQ3-native", section "What TQ3 actually does"):
+// the block is multiplied by D1 before the butterflies and its rotated values
+// by D2, and the stored norm is the fp32 shape-gain n / (rho / sqrt(128)), rho
+// the norm of the selected centroids.
+template <int BITS, int FIELD, bool TQ = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_quantize_kernel(const WeightGroup g) {
+  static_assert(!TQ || (BITS == 3 && FIELD == 3), "TQ3 stores packed 3-bit codes");
   // one LDS array: the entry table at offset 0 (so its reads need no base
-  // add), the bucket table, then the 256-byte aligned per-wave stages
-  constexpr int kTab = 256 + HLWQ_BUCKETS;
+  // add), the bucket table, TQ3's pair-square table, then the 256-byte
+  // aligned per-wave stages
+  constexpr int kSq = 256 + HLWQ_BUCKETS;
+  constexpr int kTab = kSq + (TQ ? 256 : 0);
   __shared__ __attribute__((aligned(256))) uint8_t lds[kTab + kWaves * kStage];
   uint32_t* tab = reinterpret_cast<uint32_t*>(lds);
   uint8_t* stage_all = lds + kTab;
@@ -547,6 +625,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   const uint32_t* src_entry = (BITS == 5) ? c_entry5 : c_entry3;
   for (int i = threadIdx.x; i < HLWQ_BUCKETS / 4; i += kThreads) tab[64 + i] = src_bucket[i];
   if (threadIdx.x < 2 * (1 << BITS)) tab[threadIdx.x] = src_entry[threadIdx.x];
+  if constexpr (TQ) fill_pair_squares<BITS>(reinterpret_cast<float*>(lds + kSq), c_cent3);
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -578,9 +657,22 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     }
 
     const NormInfo ni = norm_info(sumsq_tree(x));
+    SignBits d2{};
+    if constexpr (TQ) {
+      const SignBits d1 = per_batch(g.tq.d1);
+      d2 = per_batch(g.tq.d2);
+#pragma unroll
+      for (int i = 0; i < kBlock; ++i) x[i] = __uint_as_float(__float_as_uint(x[i]) ^ sign_bit(d1, i));
+    }
     fwht(x);
     uint32_t words[4 * FIELD];
-    encode<FIELD, kBlock>(x, ni.r, lds, 256u, __uint_as_float(HLWQ_BUCKET_BIAS), words);
+    encode<FIELD, kBlock, TQ>(x, ni.r, lds, 256u, __uint_as_float(HLWQ_BUCKET_BIAS), words, d2);
+    float gain = 0.0f;
+    if constexpr (TQ) {
+      // RN(1 / sqrt(128)) = RN(sqrt(2)) / 16
+      const float t = sqrtf(recon_sumsq<BITS, kBlock>(words, lds + kSq)) * 0x1.6a09e6p-4f;
+      gain = ni.n / t;
+    }
 
     // the codes of the batch are contiguous: kOut bytes per block
 #pragma unroll
@@ -589,12 +681,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       *reinterpret_cast<u32x4*>(stage + kOut * lane + 16 * q) = v;
     }
     stage_out<FIELD, false>(g.packed[d] + static_cast<size_t>(p.g0) * kOut, p.nvalid * kOut, stage, lane, sl);
-    if (static_cast<uint32_t>(lane) < p.nvalid) g.norms[d][p.lb] = ni.n16;
+    if (static_cast<uint32_t>(lane) < p.nvalid) {
+      if constexpr (TQ) static_cast<float*>(g.norms[d])[p.lb] = gain;
+      else static_cast<uint16_t*>(g.norms[d])[p.lb] = ni.n16;
+    }
   }
 }
 
-template <int BITS, int FIELD>
+// TQ: TQ3's inverse: D2 mirrors the codes, the butterflies run as for HLWQ,
+// the scale is the fp32 shape-gain / 128 and D1 negates the bf16 results.
+template <int BITS, int FIELD, bool TQ = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_dequantize_kernel(const WeightGroup g) {
+  static_assert(!TQ || (BITS == 3 && FIELD == 3), "TQ3 stores packed 3-bit codes");
   // one LDS array: the centroid pair table at offset 0, then the per-wave stages
   constexpr int kPairs = 8 << (2 * BITS);
   __shared__ __attribute__((aligned(256))) uint8_t lds[kPairs + kWaves * kStage];
@@ -615,7 +713,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     const BatchPos p = batch_pos(g, d, b, lane);
 
     stage_in<FIELD, false, 0>(g.packed[d] + static_cast<size_t>(p.g0) * kIn, p.nvalid * kIn, stage, lane, sl);
-    const float scale = f16_value(g.norms[d][p.lb]) * 0x1p-7f;
+    float nv;
+    if constexpr (TQ) nv = static_cast<const float*>(g.norms[d])[p.lb];
+    else nv = f16_value(static_cast<const uint16_t*>(g.norms[d])[p.lb]);
+    const float scale = nv * 0x1p-7f;
     wait_vmem();
     // lanes past the end of the batch read (and later write) the last block
     const uint32_t slot = p.lb - p.g0;
@@ -628,6 +729,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       words[4 * q + 2] = v.z;
       words[4 * q + 3] = v.w;
     }
+    SignBits d1{};
+    if constexpr (TQ) {
+      d1 = per_batch(g.tq.d1);
+#pragma unroll
+      for (int q = 0; q < 4 * FIELD; ++q) words[q] ^= g.tq.flip2[q];
+    }
 
     float v[kBlock];
     if constexpr (FIELD == BITS) decode_stage1<BITS, kBlock>(words, lds, v);
@@ -635,7 +742,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     fwht<kBlock, 2>(v);
     uint32_t pk[kBlock / 2];
 #pragma unroll
-    for (int j = 0; j < kBlock; j += 2) pk[j / 2] = pack_bf16x2(v[j] * scale, v[j + 1] * scale);
+    for (int j = 0; j < kBlock; j += 2)
+      pk[j / 2] = pack_bf16x2(v[j] * scale, v[j + 1] * scale) ^ (TQ ? pair_sign_mask(d1, j / 2) : 0u);
 
     if (g.whole[d] && p.nvalid == 64u) {
       write_block_full(lane_a, pk);
@@ -1021,7 +1129,8 @@ int launch_status() {
 }
 
 // Validate one weight descriptor; *blocks = rows * nb (0 means nothing to do).
-int check_weight_desc(const hlwq_mat_desc& m, int64_t* blocks) {
+// norm_bytes: 2 (fp16 norms) or 4 (TQ3's fp32 norms).
+int check_weight_desc(const hlwq_mat_desc& m, int64_t* blocks, int norm_bytes = 2) {
   *blocks = 0;
   if (m.rows < 0 || m.in < 0) return HLWQ_ERR_SHAPE;
   if (m.rows == 0 || m.in == 0) return HLWQ_OK;
@@ -1032,7 +1141,8 @@ int check_weight_desc(const hlwq_mat_desc& m, int64_t* blocks) {
   int64_t nblk;
   if (!mul_ok(m.rows, nb, &nblk) || !mul_ok(nblk, 80, &bytes)) return HLWQ_ERR_SHAPE;
   if (nblk > 0x7fffffff) return HLWQ_ERR_LIMIT;
-  if ((reinterpret_cast<uintptr_t>(m.packed) & 15u) || (reinterpret_cast<uintptr_t>(m.norms) & 1u) ||
+  if ((reinterpret_cast<uintptr_t>(m.packed) & 15u) ||
+      (reinterpret_cast<uintptr_t>(m.norms) & static_cast<uintptr_t>(norm_bytes - 1)) ||
       (reinterpret_cast<uintptr_t>(m.w) & 1u))
     return HLWQ_ERR_ALIGN;
   *blocks = nblk;
@@ -1056,26 +1166,67 @@ uint32_t persistent_grid(uint32_t batches) {
   return static_cast<uint32_t>(want < cap ? want : cap);
 }
 
-// field: bits per stored code (bits for packed codes, 8 for one code per byte)
+// SplitMix64 (Steele, Lea & Flood, "Fast splittable pseudorandom number
+// generators", OOPSLA 2014): the state advances by the golden-ratio gamma and
+// each output is the state through the variant-13 mix (shifts 30, 27, 31).
+uint64_t splitmix64_next(uint64_t& state) {
+  state += 0x9E3779B97F4A7C15ull;
+  uint64_t z = state;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// TQ3's two 128-entry sign vectors for a seed: entry i of D1 is -1 when the
+// top bit of output i is set, entry i of D2 likewise with output 128 + i.
+// words[0..3] hold D1, words[4..7] D2 (bit i of word i / 32 for entry i).
+void tq3_sign_words(uint64_t seed, uint32_t words[8]) {
+  uint64_t state = seed;
+  for (int i = 0; i < 8; ++i) words[i] = 0;
+  for (int i = 0; i < 2 * kBlock; ++i)
+    if (splitmix64_next(state) >> 63) words[i >> 5] |= 1u << (i & 31);
+}
+
+TqSigns tq3_state(uint64_t seed) {
+  uint32_t words[8];
+  tq3_sign_words(seed, words);
+  TqSigns t;
+  std::memset(&t, 0, sizeof(t));
+  for (int i = 0; i < 4; ++i) {
+    t.d1.w[i] = words[i];
+    t.d2.w[i] = words[4 + i];
+  }
+  for (int j = 0; j < kBlock; ++j)
+    if ((words[4 + (j >> 5)] >> (j & 31)) & 1u)
+      for (int b = 3 * j; b < 3 * j + 3; ++b) t.flip2[b >> 5] |= 1u << (b & 31);
+  return t;
+}
+
+// field: bits per stored code (bits for packed codes, 8 for one code per byte);
+// tq: TQ3's quantizer state (bits 3, packed codes, fp32 norms), or NULL for HLWQ.
 template <bool QUANT>
-int run_weight_group(const hlwq_mat_desc* mats, int n, int bits, int field, hipStream_t stream) {
+int run_weight_group(const hlwq_mat_desc* mats, int n, int bits, int field, hipStream_t stream,
+                     const TqSigns* tq = nullptr) {
   if (n < 0) return HLWQ_ERR_SHAPE;
   if (n > 0 && !mats) return HLWQ_ERR_NULL;
   if (bits != 5 && bits != 3) return HLWQ_ERR_BITS;
+  if (tq && (bits != 3 || field != 3)) return HLWQ_ERR_BITS;
+  const int norm_bytes = tq ? 4 : 2;
   // validate everything before enqueuing anything
   for (int i = 0; i < n; ++i) {
     int64_t b;
-    const int st = check_weight_desc(mats[i], &b);
+    const int st = check_weight_desc(mats[i], &b, norm_bytes);
     if (st != HLWQ_OK) return st;
   }
   int i = 0;
   while (i < n) {
     WeightGroup g;
     std::memset(&g, 0, sizeof(g));
+    if (tq) g.tq = *tq;
     int64_t batches = 0;
     for (; i < n && g.n < kMaxGroup; ++i) {
       int64_t nblk;
-      check_weight_desc(mats[i], &nblk);
+      check_weight_desc(mats[i], &nblk, norm_bytes);
       if (nblk == 0) continue;
       const int k = g.n++;
       g.batch_start[k] = static_cast<uint32_t>(batches);
@@ -1084,7 +1235,7 @@ int run_weight_group(const hlwq_mat_desc* mats, int n, int bits, int field, hipS
       g.in[k] = mats[i].in;
       g.w[k] = static_cast<uint16_t*>(mats[i].w);
       g.packed[k] = static_cast<uint8_t*>(mats[i].packed);
-      g.norms[k] = static_cast<uint16_t*>(mats[i].norms);
+      g.norms[k] = mats[i].norms;
       g.staged[k] = (mats[i].in % 8 == 0) && ((reinterpret_cast<uintptr_t>(mats[i].w) & 15u) == 0);
       g.whole[k] = g.staged[k] && (mats[i].in % kBlock == 0);
       batches += ceil_div(nblk, 64);
@@ -1095,7 +1246,10 @@ int run_weight_group(const hlwq_mat_desc* mats, int n, int bits, int field, hipS
     g.total_batches = static_cast<uint32_t>(batches);
     const dim3 grid(persistent_grid(g.total_batches)), block(kThreads);
     const bool bytes = field == 8;
-    if (QUANT) {
+    if (tq) {
+      if (QUANT) hipLaunchKernelGGL((hlwq_quantize_kernel<3, 3, true>), grid, block, 0, stream, g);
+      else hipLaunchKernelGGL((hlwq_dequantize_kernel<3, 3, true>), grid, block, 0, stream, g);
+    } else if (QUANT) {
       if (bits == 5) {
         if (bytes) hipLaunchKernelGGL((hlwq_quantize_kernel<5, 8>), grid, block, 0, stream, g);
         else hipLaunchKernelGGL((hlwq_quantize_kernel<5, 5>), grid, block, 0, stream, g);
@@ -1288,6 +1442,40 @@ int hlwq_dequantize_codes8(const void* codes_u8, const void* norms_f16, int64_t 
   const int st = make_single(w_bf16_out, codes_u8, norms_f16, n_mats, out, in, block, bits, &m);
   if (st != HLWQ_OK) return st;
   return run_weight_group<false>(&m, 1, bits, 8, static_cast<hipStream_t>(hip_stream));
+}
+
+int hlwq_tq3_signs(uint64_t seed, uint32_t* sign_words) {
+  if (!sign_words) return HLWQ_ERR_NULL;
+  tq3_sign_words(seed, sign_words);
+  return HLWQ_OK;
+}
+
+int hlwq_tq3_quantize(const void* w_bf16, int64_t n_mats, int64_t out, int64_t in, int group, uint64_t seed,
+                      void* packed_u8, void* norms_f32, void* hip_stream) {
+  hlwq_mat_desc m;
+  const int st = make_single(w_bf16, packed_u8, norms_f32, n_mats, out, in, group, 3, &m);
+  if (st != HLWQ_OK) return st;
+  const TqSigns tq = tq3_state(seed);
+  return run_weight_group<true>(&m, 1, 3, 3, static_cast<hipStream_t>(hip_stream), &tq);
+}
+
+int hlwq_tq3_dequantize(const void* packed_u8, const void* norms_f32, int64_t n_mats, int64_t out, int64_t in,
+                        int group, uint64_t seed, void* w_bf16_out, void* hip_stream) {
+  hlwq_mat_desc m;
+  const int st = make_single(w_bf16_out, packed_u8, norms_f32, n_mats, out, in, group, 3, &m);
+  if (st != HLWQ_OK) return st;
+  const TqSigns tq = tq3_state(seed);
+  return run_weight_group<false>(&m, 1, 3, 3, static_cast<hipStream_t>(hip_stream), &tq);
+}
+
+int hlwq_tq3_quantize_grouped(const hlwq_mat_desc* mats, int n, uint64_t seed, void* hip_stream) {
+  const TqSigns tq = tq3_state(seed);
+  return run_weight_group<true>(mats, n, 3, 3, static_cast<hipStream_t>(hip_stream), &tq);
+}
+
+int hlwq_tq3_dequantize_grouped(const hlwq_mat_desc* mats, int n, uint64_t seed, void* hip_stream) {
+  const TqSigns tq = tq3_state(seed);
+  return run_weight_group<false>(mats, n, 3, 3, static_cast<hipStream_t>(hip_stream), &tq);
 }
 
 int hlwq_kv_quantize(const void* kv_bf16, int64_t batch, int64_t heads, int64_t tokens, int head_dim, int bits,
