@@ -46,8 +46,10 @@ Tier D (fp64) is the definition; tier C (fp32) fixes one operation order:
              z = butterflies (strides 1, 2, ..., 64) of D1 x (exact sign flips);
              y = D2 RN(z r)  (exact sign flips);
              code = number of fp32 thresholds strictly below y;
-             e = RN(c[code]^2); rho2 = adjacent-pair tree of e whose level 0 is
-             RN(e_2j + e_2j+1); rho = correctly rounded sqrt;
+             e = RN(c[code]^2); rho2 = the exact sum of the 128 e values,
+             rounded once to fp32 (the sum of squares has no order of its
+             own; this one does not depend on any); rho = correctly rounded
+             sqrt;
              t = RN(rho * RN(1 / sqrt(128))); g = RN(n / t).
   dequant :  v = D2 c[code]; z = butterflies of v; s = RN(g * 2^-7);
              out = bf16_RNE(D1 RN(z s)).
@@ -135,11 +137,15 @@ def dequantize_def(codes: np.ndarray, g: np.ndarray, d1: np.ndarray, d2: np.ndar
 # --------------------------------------------------------------------------
 
 def recon_sumsq_f32(codes: np.ndarray, c32: np.ndarray) -> np.ndarray:
-    """rho^2 of tier C: squares e = RN(c^2) summed by the adjacent-pair tree."""
+    """rho^2 of tier C: the squares e = RN(c^2), summed exactly, rounded once.
+
+    Every e is an fp32 value in [c_min^2, c_max^2] ~ [0.06, 4.64], a multiple of
+    2^-28, and 128 of them sum to less than 2^10, so every partial sum is a
+    multiple of 2^-28 below 2^10: 38 significant bits, exact in fp64.  The fp64
+    sum is therefore the exact sum, and its conversion the one rounding.
+    """
     e = (c32 * c32).astype(np.float32)[np.asarray(codes)]
-    while e.shape[-1] > 1:
-        e = (e[..., 0::2] + e[..., 1::2]).astype(np.float32)
-    return e[..., 0]
+    return np.sum(e.astype(np.float64), axis=-1).astype(np.float32)
 
 
 def quantize_groups_c(x: np.ndarray, d1: np.ndarray, d2: np.ndarray):

@@ -187,6 +187,21 @@ def test_matrix_tail_group_is_zero_padded():
     assert np.sum(err.astype(np.float64) ** 2) < 0.06 * np.sum(ref.bf16_to_f32(w).astype(np.float64) ** 2)
 
 
+def test_reconstruction_sum_is_exactly_rounded():
+    # the fp64 sum of the squared centroids equals the exactly rounded sum
+    # (math.fsum), on codes drawn uniformly and on the extremes
+    c32 = lm.table(3)[0]
+    rng = np.random.default_rng(12)
+    codes = rng.integers(0, 8, (500, 128))
+    codes[0] = 0
+    codes[1] = 3
+    codes[2] = np.arange(128) % 8
+    got = tq.recon_sumsq_f32(codes, c32)
+    e = (c32 * c32).astype(np.float32)
+    for row, g in zip(codes, got):
+        assert g == np.float32(math.fsum(float(e[k]) for k in row))
+
+
 def test_kappa_is_the_rounded_inverse_sqrt():
     # RN(1 / sqrt(128)) = RN(sqrt(2)) / 16 (a power-of-two scaling is exact)
     assert np.float32(1.0 / math.sqrt(128)) == np.float32(math.sqrt(2.0)) / np.float32(16)
