@@ -9,7 +9,8 @@
 //   * the decision thresholds: the largest fp32 value not above the exact
 //     midpoint of two neighbouring fp32 centroids, so "number of thresholds
 //     strictly below y" is the index of the nearest centroid, ties low;
-//   * the two tables the kernels use to find a code with one compare.
+//   * the two tables the kernels use to find a code with one compare;
+//   * for Q3, the same two tables for the mirrored search of TQ3 (below).
 //
 // Bucket search.  For a rotated value y the kernels form, in fp32,
 //   u = fma(y, 2^-146, bias)       bias = C * 2^-149, a denormal, C even
@@ -28,6 +29,17 @@
 // against the plain count on every fp32 value near every threshold and bucket
 // edge, plus a dense sweep, and exits non-zero (failing the build) on any
 // disagreement.
+//
+// Mirrored search (TQ3's output signs).  TQ3 codes -y where its sign vector
+// D2 is -1.  The Q3 thresholds T are symmetric (t_k = -t_{K-2-k} exactly, as
+// the centroids are), so for every fp32 y
+//   #{t in T : t < -y} = #{t in T : t > y} = (K - 1) - #{t in T : t <= y}
+//                      = (K - 1) - #{t' in T' : t' < y},  T' = {pred(t)},
+// pred(t) the next fp32 value below t (t <= y iff pred(t) < y for fp32 y).
+// So the code of -y is K - 1 - (the code of y searched among T'), and K - 1 - c
+// = c ^ (K - 1): a bucket search over T' (bias C + number of buckets, its
+// tables stored after the plain ones) plus one xor of the packed codes.  This
+// program checks the symmetry and verifies that identity by brute force.
 //
 // Reach.  Let S be the exact squared norm of a block and s the computed one.
 // Each of the R roundings of the norm sum (191 for a 128-block, 383 for a
@@ -208,6 +220,66 @@ Tables make_tables(int K, int buckets) {
   return tb;
 }
 
+// The search tables over T' = {pred(t)} of a symmetric threshold set (see
+// "Mirrored search" above), verified against the plain count of -y.
+Tables mirror_tables(const Tables& tb) {
+  const int K = tb.K;
+  for (int k = 0; k + 1 < K; ++k) {
+    if (tb.thr[k] != -tb.thr[K - 2 - k]) {
+      std::fprintf(stderr, "gen_tables: thresholds not symmetric (K=%d)\n", K);
+      std::exit(1);
+    }
+  }
+  Tables m;
+  m.K = K;
+  m.cent = tb.cent;
+  for (float t : tb.thr) m.thr.push_back(std::nextafterf(t, -INFINITY));
+  const int buckets = (int)tb.bucket.size(), C = buckets / 2;
+  m.bias = tb.bias;
+  for (int k = 0; k < buckets; ++k) {
+    const double lo = (k - C - 0.5) / 8.0, hi = (k - C + 0.5) / 8.0;
+    int base = 0, inside = 0;
+    for (float t : m.thr) {
+      if ((double)t < lo) ++base;
+      else if ((double)t < hi) ++inside;
+    }
+    if (inside > 1) {
+      std::fprintf(stderr, "gen_tables: mirrored bucket %d holds %d thresholds\n", k, inside);
+      std::exit(1);
+    }
+    m.bucket.push_back((uint8_t)(8 * base));
+  }
+  for (int b = 0; b < K; ++b) {
+    m.entry.push_back(b + 1 < K ? f2u(m.thr[b]) : f2u(INFINITY));
+    m.entry.push_back((uint32_t)b);
+  }
+  const float ymax = (float)(buckets / 16.0 - 0.125);
+  auto check = [&](float y) {
+    if (!(std::fabs(y) < ymax)) return;
+    if ((bucket_code(m, y) ^ (uint32_t)(K - 1)) != count_code(tb.thr, -y)) {
+      std::fprintf(stderr, "gen_tables: mirrored search wrong at y=%a\n", y);
+      std::exit(1);
+    }
+  };
+  std::vector<float> probes;
+  for (float t : tb.thr) probes.push_back(t);
+  for (int k = 0; k <= buckets; ++k) probes.push_back((float)((k - C - 0.5) / 8.0));
+  probes.push_back(0.0f);
+  for (float p : probes) {
+    float lo = p, hi = p;
+    for (int i = 0; i < 4096; ++i) {
+      lo = std::nextafterf(lo, -INFINITY);
+      hi = std::nextafterf(hi, INFINITY);
+      check(lo);
+      check(hi);
+      check(p);
+    }
+  }
+  for (int64_t i = -20000000; i <= 20000000; ++i) check((float)((double)i * (ymax / 20000000.0)));
+  for (float y : {0.0f, -0.0f, 0x1p-149f, -0x1p-149f, 0x1p-126f, -0x1p-126f}) check(y);
+  return m;
+}
+
 void emit_floats(const char* name, const std::vector<float>& v) {
   std::printf("#define %s { \\\n", name);
   for (size_t i = 0; i < v.size(); ++i)
@@ -240,6 +312,9 @@ int main() {
   const Tables q3 = make_tables(8, 2048);
   const Tables kv3 = make_tables(8, 4096);
   const Tables kv2 = make_tables(4, 4096);
+  Tables q3m = mirror_tables(q3);
+  // the mirrored entries follow the plain ones (K entries of 8 bytes)
+  for (uint8_t& b : q3m.bucket) b = (uint8_t)(b + 8 * q3.K);
   std::printf("// Generated at build time by gen_tables.cpp: Lloyd-Max tables for N(0,1).\n");
   std::printf("#pragma once\n");
   std::printf("#define HLWQ_SEARCH_SCALE %af\n", (double)kScale);
@@ -253,6 +328,8 @@ int main() {
   emit_floats("HLWQ_THRESHOLDS_3", q3.thr);
   emit_bytes("HLWQ_BUCKET_3", q3.bucket);
   emit_words("HLWQ_ENTRY_3", q3.entry);
+  emit_bytes("HLWQ_BUCKET_3M", q3m.bucket);
+  emit_words("HLWQ_ENTRY_3M", q3m.entry);
   emit_bytes("HLWQ_KV_BUCKET_3", kv3.bucket);
   emit_floats("HLWQ_CENTROIDS_2", kv2.cent);
   emit_floats("HLWQ_THRESHOLDS_2", kv2.thr);

@@ -53,6 +53,8 @@ __constant__ uint32_t c_bucket3[HLWQ_BUCKETS / 4] = HLWQ_BUCKET_3;
 __constant__ uint32_t c_kvbucket3[HLWQ_KV_BUCKETS / 4] = HLWQ_KV_BUCKET_3;
 __constant__ uint32_t c_entry5[2 * 32] = HLWQ_ENTRY_5;
 __constant__ uint32_t c_entry3[2 * 8] = HLWQ_ENTRY_3;
+__constant__ uint32_t c_bucket3m[HLWQ_BUCKETS / 4] = HLWQ_BUCKET_3M;  // TQ3's mirrored search
+__constant__ uint32_t c_entry3m[2 * 8] = HLWQ_ENTRY_3M;
 __constant__ float c_cent2[4] = HLWQ_CENTROIDS_2;
 __constant__ uint32_t c_entry2[2 * 4] = HLWQ_ENTRY_2;
 __constant__ uint32_t c_kvbucket2[HLWQ_KV_BUCKETS / 4] = HLWQ_KV_BUCKET_2;
@@ -243,10 +245,9 @@ __device__ __forceinline__ uint32_t pair_sign_mask(const SignBits& s, int m) {
 // entry table at LDS offset 0, and the code is base + (y > threshold).  The
 // table generator proves this equals the number of fp32 thresholds strictly
 // below y for every reachable y.
-// `flip` (0 or the sign bit) negates y first: TQ3's output sign vector.
-__device__ __forceinline__ uint32_t code_of(float z, float r, uint32_t flip, const uint8_t* __restrict__ lds,
-                                            uint32_t bucket, float bias) {
-  const float y = __uint_as_float(__float_as_uint(z * r) ^ flip);
+__device__ __forceinline__ uint32_t code_of(float z, float r, const uint8_t* __restrict__ lds, uint32_t bucket,
+                                            float bias) {
+  const float y = z * r;
   const uint32_t k = __float_as_uint(__builtin_fmaf(y, HLWQ_SEARCH_SCALE, bias));
   const uint32_t e = lds[bucket + k];
   const uint2 v = *reinterpret_cast<const uint2*>(lds + e);
@@ -258,13 +259,19 @@ __device__ __forceinline__ uint32_t code_of(float z, float r, uint32_t flip, con
 // bit string.  Words are built top-down by Horner steps acc = (acc << BITS) +
 // code; a code that straddles two words is computed once, finishes the upper
 // word's bottom bits and starts the lower word.
-// With FLIP, the y of value j is negated where bit j of the 128-bit string
-// `s2` is set (TQ3's D2).
-template <int BITS, int L, bool FLIP = false>
+// With MIRROR (TQ3's D2, 3-bit codes), value j whose bit in the 128-bit
+// string s2 is set is searched in the mirrored tables, which follow the plain
+// bucket table (bias + HLWQ_BUCKETS), and gives 7 - code(-y); the caller
+// turns it into code(-y) with an xor of the packed words.
+template <int BITS, int L, bool MIRROR = false>
 __device__ __forceinline__ void encode(const float (&z)[L], float r, const uint8_t* __restrict__ lds, uint32_t bucket,
                                        float bias, uint32_t (&w)[L * BITS / 32], const SignBits& s2 = SignBits{}) {
   constexpr int W = L * BITS / 32;
-  auto code = [&](int j) { return code_of(z[j], r, FLIP ? sign_bit(s2, j) : 0u, lds, bucket, bias); };
+  static_assert(HLWQ_BUCKETS == 2048, "sign_bit >> 20 selects the mirrored bucket table");
+  auto code = [&](int j) {
+    const float b = MIRROR ? __uint_as_float(__float_as_uint(bias) + (sign_bit(s2, j) >> 20)) : bias;
+    return code_of(z[j], r, lds, bucket, b);
+  };
   uint32_t carry = 0;  // straddling code shared with the word below
 #pragma unroll
   for (int wi = W - 1; wi >= 0; --wi) {
@@ -333,29 +340,36 @@ __device__ __forceinline__ void decode_bytes_stage1(const uint32_t (&w)[L / 4], 
   }
 }
 
-// Squared norm of the centroids a block's codes select, by the adjacent-pair
-// tree: level 0 is read from a table (LDS offset `sq`) holding, for every
-// 2*BITS-bit pair index i with a = i mod 2^BITS and b = i >> BITS,
-// RN(RN(c[a]^2) + RN(c[b]^2)); every further level adds neighbouring sums.
-template <int BITS, int L>
-__device__ __forceinline__ float recon_sumsq(const uint32_t (&w)[L * BITS / 32], const uint8_t* __restrict__ sq) {
-  float s[L / 2];
+// Squared norm of the 8-centroid codes a block selects, summed exactly and
+// rounded once.  c is symmetric, so c[k]^2 depends only on the magnitude
+// class m of code k = (b2 b1 b0): m = 2 (b1 XNOR b2) + (b0 XNOR b2), c[4 + m]
+// for b2 = 1 and c[3 - m] = -c[4 + m] for b2 = 0.  Three popcounts over the
+// 384-bit code string give A = #(b1 XNOR b2), B = #(b0 XNOR b2) and
+// C = #(both); the class counts are then N3 = C, N2 = A - C, N1 = B - C,
+// N0 = 128 - A - B + C.  Every RN(c^2) is a multiple of 2^-28 and the total is
+// below 2^10, so the fp64 products and sum are exact and the conversion to
+// fp32 is the one rounding.  Per word: two funnel shifts bring b1 and b2 of
+// every code onto its b0 position; the masks pick the b0 positions of the
+// word (period 3 words, as 32 = 2 mod 3).
+__device__ __forceinline__ float recon_sumsq3(const uint32_t (&w)[12]) {
+  constexpr uint32_t kB0[3] = {0x49249249u, 0x92492492u, 0x24924924u};
+  constexpr float cent[8] = HLWQ_CENTROIDS_3;
+  constexpr float c4 = cent[4], c5 = cent[5], c6 = cent[6], c7 = cent[7];
+  uint32_t a = 0, b = 0, c = 0;
 #pragma unroll
-  for (int m = 0; m < L / 2; ++m) s[m] = *reinterpret_cast<const float*>(sq + pair_offset<BITS, 2>(w, m));
-#pragma unroll
-  for (int k = L / 4; k >= 1; k >>= 1)
-#pragma unroll
-    for (int i = 0; i < k; ++i) s[i] = s[2 * i] + s[2 * i + 1];
-  return s[0];
-}
-
-template <int BITS>
-__device__ __forceinline__ void fill_pair_squares(float* sq, const float* __restrict__ cent) {
-  constexpr int K = 1 << BITS;
-  for (int i = threadIdx.x; i < K * K; i += kThreads) {
-    const float a = cent[i & (K - 1)], b = cent[i >> BITS];
-    sq[i] = a * a + b * b;
+  for (int q = 0; q < 12; ++q) {
+    const uint32_t next = q + 1 < 12 ? w[q + 1] : 0u;
+    const uint32_t t1 = __builtin_amdgcn_alignbit(next, w[q], 1);  // b1 at b0
+    const uint32_t t2 = __builtin_amdgcn_alignbit(next, w[q], 2);  // b2 at b0
+    const uint32_t m0 = ~(w[q] ^ t2) & kB0[q % 3];
+    const uint32_t m1 = ~(t1 ^ t2) & kB0[q % 3];
+    b += __builtin_popcount(m0);
+    a += __builtin_popcount(m1);
+    c += __builtin_popcount(m0 & m1);
   }
+  const double e0 = (double)(c4 * c4), e1 = (double)(c5 * c5), e2 = (double)(c6 * c6), e3 = (double)(c7 * c7);
+  const double s = (double)(128u - a - b + c) * e0 + (double)(b - c) * e1 + (double)(a - c) * e2 + (double)c * e3;
+  return (float)s;
 }
 
 // Fill the pair table of a K-centroid codebook (K * K entries of 8 bytes).
@@ -523,6 +537,24 @@ __device__ __forceinline__ void read_block_full(uint32_t a, float (&x)[kBlock]) 
   for (int c = 0; c < 16; ++c) unpack8(lds_read16(a ^ (16u * c)), x, c);
 }
 
+// The same with TQ3's D1 applied at no extra cost: the low bf16 of a word
+// becomes (w << 16) + sign (adding 2^31 to a value whose low 16 bits are zero
+// flips bit 31 and nothing else) and the high one (w & 0xffff0000) ^ sign, one
+// instruction each, as without the signs.
+__device__ __forceinline__ void read_block_full_signed(uint32_t a, float (&x)[kBlock], const SignBits& d1) {
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const u32x4 v = lds_read16(a ^ (16u * c));
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = 8 * c + 2 * q;
+      x[j] = __uint_as_float((w[q] << 16) + sign_bit(d1, j));
+      x[j + 1] = __uint_as_float((w[q] & 0xffff0000u) ^ sign_bit(d1, j + 1));
+    }
+  }
+}
+
 __device__ __forceinline__ void write_block_full(uint32_t a, const uint32_t (&pk)[kBlock / 2]) {
 #pragma unroll
   for (int c = 0; c < 16; ++c) {
@@ -560,6 +592,42 @@ struct TqSigns {
   SignBits d1, d2;
   uint32_t flip2[12];
 };
+
+// SplitMix64 (Steele, Lea & Flood, "Fast splittable pseudorandom number
+// generators", OOPSLA 2014): the state advances by the golden-ratio gamma and
+// each output is the state through the variant-13 mix (shifts 30, 27, 31).
+constexpr uint64_t splitmix64_next(uint64_t& state) {
+  state += 0x9E3779B97F4A7C15ull;
+  uint64_t z = state;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// TQ3's state for a seed: entry i of D1 is -1 when the top bit of output i is
+// set, entry i of D2 likewise with output 128 + i.
+constexpr TqSigns tq3_state(uint64_t seed) {
+  TqSigns t{};
+  uint64_t state = seed;
+  for (int i = 0; i < 2 * kBlock; ++i) {
+    if (splitmix64_next(state) >> 63) {
+      SignBits& d = i < kBlock ? t.d1 : t.d2;
+      const int e = i & (kBlock - 1);
+      d.w[e >> 5] |= 1u << (e & 31);
+    }
+  }
+  for (int j = 0; j < kBlock; ++j)
+    if ((t.d2.w[j >> 5] >> (j & 31)) & 1u)
+      for (int b = 3 * j; b < 3 * j + 3; ++b) t.flip2[b >> 5] |= 1u << (b & 31);
+  return t;
+}
+
+// The format's recorded quantizer state (seed 42, "Qwen3.6-35B-A3B-TQ3-native",
+// section "Files"), compiled into its own kernels: every sign is then a
+// constant and costs nothing (a negation folds into the instruction that reads
+// the value, a table choice into an immediate).
+constexpr uint64_t kTq3Seed = 42;
+constexpr TqSigns kTq3Seed42 = tq3_state(kTq3Seed);
 
 struct WeightGroup {
   int32_t n;                           // matrices in this launch
@@ -609,15 +677,15 @@ __device__ __forceinline__ BatchPos batch_pos(const WeightGroup& g, int d, uint3
 // TQ: TQ3 ("Qwen3.6-35B-A3B-TQ3-native", section "What TQ3 actually does"):
 // the block is multiplied by D1 before the butterflies and its rotated values
 // by D2, and the stored norm is the fp32 shape-gain n / (rho / sqrt(128)), rho
-// the norm of the selected centroids.
-template <int BITS, int FIELD, bool TQ = false>
+// the norm of the selected centroids.  TQ = 1 takes the signs from the launch
+// arguments, TQ = 2 is the compiled-in seed-42 state.
+template <int BITS, int FIELD, int TQ = 0>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_quantize_kernel(const WeightGroup g) {
   static_assert(!TQ || (BITS == 3 && FIELD == 3), "TQ3 stores packed 3-bit codes");
   // one LDS array: the entry table at offset 0 (so its reads need no base
   // add), the bucket table, TQ3's pair-square table, then the 256-byte
   // aligned per-wave stages
-  constexpr int kSq = 256 + HLWQ_BUCKETS;
-  constexpr int kTab = kSq + (TQ ? 256 : 0);
+  constexpr int kTab = 256 + (TQ ? 2 : 1) * HLWQ_BUCKETS;
   __shared__ __attribute__((aligned(256))) uint8_t lds[kTab + kWaves * kStage];
   uint32_t* tab = reinterpret_cast<uint32_t*>(lds);
   uint8_t* stage_all = lds + kTab;
@@ -625,7 +693,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   const uint32_t* src_entry = (BITS == 5) ? c_entry5 : c_entry3;
   for (int i = threadIdx.x; i < HLWQ_BUCKETS / 4; i += kThreads) tab[64 + i] = src_bucket[i];
   if (threadIdx.x < 2 * (1 << BITS)) tab[threadIdx.x] = src_entry[threadIdx.x];
-  if constexpr (TQ) fill_pair_squares<BITS>(reinterpret_cast<float*>(lds + kSq), c_cent3);
+  if constexpr (TQ) {
+    // the mirrored entries at byte 64, the mirrored buckets after the plain ones
+    for (int i = threadIdx.x; i < HLWQ_BUCKETS / 4; i += kThreads) tab[64 + HLWQ_BUCKETS / 4 + i] = c_bucket3m[i];
+    if (threadIdx.x < 16) tab[16 + threadIdx.x] = c_entry3m[threadIdx.x];
+  }
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -640,37 +712,50 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     const int d = group_of(g, b);
     const BatchPos p = batch_pos(g, d, b, lane);
 
+    // TQ3's sign vectors (D1 is applied while the block is read; squares, and
+    // so the norm, do not see it)
+    SignBits d1{}, d2{};
+    if constexpr (TQ == 1) {
+      d1 = per_batch(g.tq.d1);
+      d2 = per_batch(g.tq.d2);
+    } else if constexpr (TQ == 2) {
+      d1 = kTq3Seed42.d1;
+      d2 = kTq3Seed42.d2;
+    }
     float x[kBlock];
     if (g.whole[d] && p.nvalid == 64u) {
       stage_in_full(batch_rsrc(g.w[d] + static_cast<int64_t>(p.g0) * kBlock, 64u * 2u * kBlock), stage, sl);
       wait_vmem();
-      read_block_full(lane_a, x);
-    } else if (g.staged[d]) {
-      const int64_t e0 = first_lane64(p.e);
-      const uint32_t off = static_cast<uint32_t>(p.e - e0) * 2u;
-      const uint32_t end = __builtin_amdgcn_readlane(off + 2u * p.n, p.nvalid - 1);
-      stage_in<16, true, kNt>(reinterpret_cast<const uint8_t*>(g.w[d] + e0), end, stage, lane, sl);
-      wait_vmem();
-      read_staged_block(stage, off, p.n, x);
+      if constexpr (TQ != 0) read_block_full_signed(lane_a, x, d1);
+      else read_block_full(lane_a, x);
     } else {
-      load_block(g.w[d] + p.e, p.n, x);
+      if (g.staged[d]) {
+        const int64_t e0 = first_lane64(p.e);
+        const uint32_t off = static_cast<uint32_t>(p.e - e0) * 2u;
+        const uint32_t end = __builtin_amdgcn_readlane(off + 2u * p.n, p.nvalid - 1);
+        stage_in<16, true, kNt>(reinterpret_cast<const uint8_t*>(g.w[d] + e0), end, stage, lane, sl);
+        wait_vmem();
+        read_staged_block(stage, off, p.n, x);
+      } else {
+        load_block(g.w[d] + p.e, p.n, x);
+      }
+      if constexpr (TQ != 0) {
+#pragma unroll
+        for (int i = 0; i < kBlock; ++i) x[i] = __uint_as_float(__float_as_uint(x[i]) ^ sign_bit(d1, i));
+      }
     }
 
     const NormInfo ni = norm_info(sumsq_tree(x));
-    SignBits d2{};
-    if constexpr (TQ) {
-      const SignBits d1 = per_batch(g.tq.d1);
-      d2 = per_batch(g.tq.d2);
-#pragma unroll
-      for (int i = 0; i < kBlock; ++i) x[i] = __uint_as_float(__float_as_uint(x[i]) ^ sign_bit(d1, i));
-    }
     fwht(x);
     uint32_t words[4 * FIELD];
-    encode<FIELD, kBlock, TQ>(x, ni.r, lds, 256u, __uint_as_float(HLWQ_BUCKET_BIAS), words, d2);
+    encode<FIELD, kBlock, TQ != 0>(x, ni.r, lds, 256u, __uint_as_float(HLWQ_BUCKET_BIAS), words, d2);
     float gain = 0.0f;
-    if constexpr (TQ) {
+    if constexpr (TQ != 0) {
+      // mirrored codes -> codes of -y
+#pragma unroll
+      for (int q = 0; q < 4 * FIELD; ++q) words[q] ^= (TQ == 2) ? kTq3Seed42.flip2[q] : g.tq.flip2[q];
       // RN(1 / sqrt(128)) = RN(sqrt(2)) / 16
-      const float t = sqrtf(recon_sumsq<BITS, kBlock>(words, lds + kSq)) * 0x1.6a09e6p-4f;
+      const float t = sqrtf(recon_sumsq3(words)) * 0x1.6a09e6p-4f;
       gain = ni.n / t;
     }
 
@@ -682,15 +767,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     }
     stage_out<FIELD, false>(g.packed[d] + static_cast<size_t>(p.g0) * kOut, p.nvalid * kOut, stage, lane, sl);
     if (static_cast<uint32_t>(lane) < p.nvalid) {
-      if constexpr (TQ) static_cast<float*>(g.norms[d])[p.lb] = gain;
+      if constexpr (TQ != 0) static_cast<float*>(g.norms[d])[p.lb] = gain;
       else static_cast<uint16_t*>(g.norms[d])[p.lb] = ni.n16;
     }
   }
 }
 
-// TQ: TQ3's inverse: D2 mirrors the codes, the butterflies run as for HLWQ,
-// the scale is the fp32 shape-gain / 128 and D1 negates the bf16 results.
-template <int BITS, int FIELD, bool TQ = false>
+// TQ: TQ3's inverse (1: signs from the launch arguments, 2: the compiled-in
+// seed-42 state): D2 mirrors the codes, the butterflies run as for HLWQ, the
+// scale is the fp32 shape-gain / 128 and D1 negates the bf16 results.
+template <int BITS, int FIELD, int TQ = 0>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_dequantize_kernel(const WeightGroup g) {
   static_assert(!TQ || (BITS == 3 && FIELD == 3), "TQ3 stores packed 3-bit codes");
   // one LDS array: the centroid pair table at offset 0, then the per-wave stages
@@ -714,7 +800,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 
     stage_in<FIELD, false, 0>(g.packed[d] + static_cast<size_t>(p.g0) * kIn, p.nvalid * kIn, stage, lane, sl);
     float nv;
-    if constexpr (TQ) nv = static_cast<const float*>(g.norms[d])[p.lb];
+    if constexpr (TQ != 0) nv = static_cast<const float*>(g.norms[d])[p.lb];
     else nv = f16_value(static_cast<const uint16_t*>(g.norms[d])[p.lb]);
     const float scale = nv * 0x1p-7f;
     wait_vmem();
@@ -730,10 +816,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       words[4 * q + 3] = v.w;
     }
     SignBits d1{};
-    if constexpr (TQ) {
+    if constexpr (TQ == 1) {
       d1 = per_batch(g.tq.d1);
 #pragma unroll
       for (int q = 0; q < 4 * FIELD; ++q) words[q] ^= g.tq.flip2[q];
+    } else if constexpr (TQ == 2) {
+      d1 = kTq3Seed42.d1;
+#pragma unroll
+      for (int q = 0; q < 4 * FIELD; ++q) words[q] ^= kTq3Seed42.flip2[q];
     }
 
     float v[kBlock];
@@ -743,7 +833,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     uint32_t pk[kBlock / 2];
 #pragma unroll
     for (int j = 0; j < kBlock; j += 2)
-      pk[j / 2] = pack_bf16x2(v[j] * scale, v[j + 1] * scale) ^ (TQ ? pair_sign_mask(d1, j / 2) : 0u);
+      pk[j / 2] = pack_bf16x2(v[j] * scale, v[j + 1] * scale) ^ (TQ != 0 ? pair_sign_mask(d1, j / 2) : 0u);
 
     if (g.whole[d] && p.nvalid == 64u) {
       write_block_full(lane_a, pk);
@@ -1166,40 +1256,13 @@ uint32_t persistent_grid(uint32_t batches) {
   return static_cast<uint32_t>(want < cap ? want : cap);
 }
 
-// SplitMix64 (Steele, Lea & Flood, "Fast splittable pseudorandom number
-// generators", OOPSLA 2014): the state advances by the golden-ratio gamma and
-// each output is the state through the variant-13 mix (shifts 30, 27, 31).
-uint64_t splitmix64_next(uint64_t& state) {
-  state += 0x9E3779B97F4A7C15ull;
-  uint64_t z = state;
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  return z ^ (z >> 31);
-}
-
-// TQ3's two 128-entry sign vectors for a seed: entry i of D1 is -1 when the
-// top bit of output i is set, entry i of D2 likewise with output 128 + i.
-// words[0..3] hold D1, words[4..7] D2 (bit i of word i / 32 for entry i).
+// The 8 sign words of hlwq_tq3_signs: D1 in words 0-3, D2 in words 4-7.
 void tq3_sign_words(uint64_t seed, uint32_t words[8]) {
-  uint64_t state = seed;
-  for (int i = 0; i < 8; ++i) words[i] = 0;
-  for (int i = 0; i < 2 * kBlock; ++i)
-    if (splitmix64_next(state) >> 63) words[i >> 5] |= 1u << (i & 31);
-}
-
-TqSigns tq3_state(uint64_t seed) {
-  uint32_t words[8];
-  tq3_sign_words(seed, words);
-  TqSigns t;
-  std::memset(&t, 0, sizeof(t));
+  const TqSigns t = tq3_state(seed);
   for (int i = 0; i < 4; ++i) {
-    t.d1.w[i] = words[i];
-    t.d2.w[i] = words[4 + i];
+    words[i] = t.d1.w[i];
+    words[4 + i] = t.d2.w[i];
   }
-  for (int j = 0; j < kBlock; ++j)
-    if ((words[4 + (j >> 5)] >> (j & 31)) & 1u)
-      for (int b = 3 * j; b < 3 * j + 3; ++b) t.flip2[b >> 5] |= 1u << (b & 31);
-  return t;
 }
 
 // field: bits per stored code (bits for packed codes, 8 for one code per byte);
@@ -1247,8 +1310,15 @@ int run_weight_group(const hlwq_mat_desc* mats, int n, int bits, int field, hipS
     const dim3 grid(persistent_grid(g.total_batches)), block(kThreads);
     const bool bytes = field == 8;
     if (tq) {
-      if (QUANT) hipLaunchKernelGGL((hlwq_quantize_kernel<3, 3, true>), grid, block, 0, stream, g);
-      else hipLaunchKernelGGL((hlwq_dequantize_kernel<3, 3, true>), grid, block, 0, stream, g);
+      // the recorded seed runs the kernels with the signs compiled in
+      const bool seed42 = std::memcmp(tq, &kTq3Seed42, sizeof(TqSigns)) == 0;
+      if (QUANT) {
+        if (seed42) hipLaunchKernelGGL((hlwq_quantize_kernel<3, 3, 2>), grid, block, 0, stream, g);
+        else hipLaunchKernelGGL((hlwq_quantize_kernel<3, 3, 1>), grid, block, 0, stream, g);
+      } else {
+        if (seed42) hipLaunchKernelGGL((hlwq_dequantize_kernel<3, 3, 2>), grid, block, 0, stream, g);
+        else hipLaunchKernelGGL((hlwq_dequantize_kernel<3, 3, 1>), grid, block, 0, stream, g);
+      }
     } else if (QUANT) {
       if (bits == 5) {
         if (bytes) hipLaunchKernelGGL((hlwq_quantize_kernel<5, 8>), grid, block, 0, stream, g);
