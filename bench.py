@@ -10,15 +10,19 @@ starts; the step's working set (5.8 GB) is far larger than the 256 MB
 Infinity Cache, so every step streams from HBM.
 
 Other workloads (--config) use the same procedure: the Gemma-4-26B-A4B-shaped
-bank, the dense hidden-5120 Linears (Q5 or --bits 3), and the H256 KV cache
-(Q3; two independent caches alternate so the working set exceeds the cache).
+bank, the dense hidden-5120 Linears (Q5 or --bits 3; dense_5120_int4 follows
+the quantize with the fused dequantize -> INT4), the H256 KV cache (Q3 or
+--bits 2; two independent caches alternate so the working set exceeds the
+cache), the streaming KV decode step (kv_h256_decode, latency-bound), and TQ3 on
+the Qwen3.6-shaped bank (qwen36_moe_bank_tq3).  --layout codes8 stores one code
+per byte.
 
 Prints one JSON line: weights/s of quantize + dequantize, with the per-kernel
 HBM roofline (algorithmic bytes / kernel time from HIP events on the launch
 stream), a measured device-to-device copy ceiling, and the CPU oracle timed
 on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 1000] [--config NAME] [--bits 5|3]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 1000] [--config NAME] [--bits 5|3|2] [--layout packed|codes8]
 """
 from __future__ import annotations
 

@@ -171,6 +171,18 @@ def test_quality_matches_max_distortion():
     assert abs(rel - mse8) < 0.1 * mse8
 
 
+def test_shape_gain_error_is_close_to_raw_norm_error():
+    # storing the raw L2 norm instead of the shape-gain: on Gaussian groups the
+    # two reconstruction errors agree to within a few percent (the shape-gain
+    # one slightly lower); the page's factor of two does not appear here
+    d1, d2 = tq.sign_vectors(42)
+    x = _gauss_groups(4096, 13).astype(np.float64)
+    codes, g, _, n = tq.quantize_def(x, d1, d2)
+    err = lambda a: np.sum((a - x) ** 2) / np.sum(x * x)
+    e_gain, e_raw = err(tq.dequantize_def(codes, g, d1, d2)), err(tq.dequantize_def(codes, n, d1, d2))
+    assert e_gain < e_raw < 1.05 * e_gain
+
+
 def test_matrix_tail_group_is_zero_padded():
     w = synth.random_bf16((3, 200), seed=11, key=2)
     packed, g = tq.quantize_c(w, 42)
