@@ -513,8 +513,8 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t*)p));
 }
-__device__ __forceinline__ u32x4 lds_read16(uint32_t a) { return *(const lds_u32x4*)a; }
-__device__ __forceinline__ void lds_write16(uint32_t a, u32x4 v) { *(lds_u32x4*)a = v; }
+__device__ __forceinline__ u32x4 lds_read16(uint32_t a) { return *(const lds_u32x4*)static_cast<uintptr_t>(a); }
+__device__ __forceinline__ void lds_write16(uint32_t a, u32x4 v) { *(lds_u32x4*)static_cast<uintptr_t>(a) = v; }
 
 // Buffer resource over `bytes` bytes at `base` (raw, unswizzled): the full
 // paths address a batch as base + per-lane VGPR offset + scalar offset, so
@@ -580,7 +580,8 @@ __device__ __forceinline__ void stage_out_full(__amdgpu_buffer_rsrc_t dst, uint3
 // A wave works on batches of 64 consecutive blocks of one matrix, one block
 // per lane.  Blocks are numbered row-major, so a batch covers one contiguous
 // byte range of W (rows are contiguous; a tail block holds only its real
-// columns).  The workgroups loop over batches (persistent grid).
+// columns).  Quantize workgroups loop over batches (persistent grid);
+// dequantize workgroups each own a run of consecutive batches (batch_range).
 // ---------------------------------------------------------------------------
 
 // TQ3's quantizer state for a launch: the two sign vectors, and D2 once more
