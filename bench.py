@@ -360,7 +360,7 @@ def decode_main(args, bits):
                    "vectors_per_step": vectors},
         "append": {"ms": round(float(ms.mean()), 4), "ms_median": round(float(np.median(ms)), 4),
                    "ms_min": round(float(ms.min()), 4), "ms_max": round(float(ms.max()), 4)},
-        "roofline": {"bound": "hbm", "kernel": "hlwq_kv_append_kernel", "achieved":
+        "roofline": {"bound": "hbm", "kernel": "hlwq_kv_append_small_kernel (one wave per head)", "achieved":
                      round(nbytes / (ms.mean() * 1e-3) / 1e9, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(nbytes / (ms.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS, 6), "traffic": None,
                      "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": round(float(ms.mean()), 4),

@@ -1231,6 +1231,120 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
   }
 }
 
+// Streaming KV append, latency path for a few new tokens per head (a decode
+// step).  The batch kernel above spends a lane pair on every encoded vector,
+// so one token per head would leave 62 of 64 lanes idle and run the whole
+// transform serially.  Here one wave encodes one vector at a time with four
+// values per lane (lane l holds values 4l .. 4l+3): the norm tree and the
+// butterflies finish across lanes (xor shuffles; fp32 addition is
+// commutative, so each step is exactly the canonical pairwise sum), and the
+// code is the plain count of thresholds below y, which needs no LDS table and
+// so no table fill before the first load.  The new tokens that stay in the
+// window are loaded at the start and written to the ring last, after every
+// ring read of the call has returned.  One wave per head.
+constexpr int kSmallAppend = 8;  // new tokens per head handled by the latency path
+
+__device__ __forceinline__ float shfl_xor(float v, int d) { return __shfl_xor(v, d, 64); }
+__device__ __forceinline__ uint32_t shfl_xor(uint32_t v, int d) {
+  return static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), d, 64));
+}
+
+template <int BITS>
+__device__ __forceinline__ void append_encode_wave(const KvAppendArgs& a, uint32_t bhi, int64_t o, uint2 w, int lane) {
+  constexpr int K = 1 << BITS;
+  constexpr float thr3[7] = HLWQ_THRESHOLDS_3;
+  constexpr float thr2[3] = HLWQ_THRESHOLDS_2;
+  float x[4] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+  // norm: level 0 (two fused pairs) and level 1 in the lane, levels 2..7 across lanes
+  float s = __builtin_fmaf(x[0], x[0], x[1] * x[1]) + __builtin_fmaf(x[2], x[2], x[3] * x[3]);
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) s = s + shfl_xor(s, d);
+  const NormInfo ni = norm_info(s);
+  // butterflies at strides 1 and 2 in the lane, 4 .. 128 across lanes
+  {
+    const float a0 = x[0] + x[1], a1 = x[0] - x[1], a2 = x[2] + x[3], a3 = x[2] - x[3];
+    x[0] = a0 + a2;
+    x[2] = a0 - a2;
+    x[1] = a1 + a3;
+    x[3] = a1 - a3;
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const bool upper = (lane & d) != 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float q = shfl_xor(x[j], d);
+      x[j] = upper ? q - x[j] : x[j] + q;
+    }
+  }
+  // codes: the number of thresholds strictly below y
+  uint32_t f = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float y = x[j] * ni.r;
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k) c += (y > (BITS == 3 ? thr3[k] : thr2[k])) ? 1u : 0u;
+    f |= c << (BITS * j);
+  }
+  constexpr uint32_t kVec = 32 * BITS;
+  const int64_t vec = static_cast<int64_t>(bhi) * a.capacity + o;
+  uint8_t* dst = a.packed + vec * kVec;
+  if constexpr (BITS == 2) {
+    dst[lane] = static_cast<uint8_t>(f);  // 4 codes of 2 bits: one byte per lane
+  } else {
+    // 8 lanes hold 32 codes = 96 bits = 3 words: place the lane's 12 bits at
+    // bit 12 i of its group's string and or the group together
+    const int i = lane & 7;
+    const int bit = 12 * i;
+    const uint64_t v = static_cast<uint64_t>(f) << (bit & 31);
+    uint32_t wd[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+      wd[k] = ((bit >> 5) == k ? static_cast<uint32_t>(v) : 0u) | ((bit >> 5) + 1 == k ? static_cast<uint32_t>(v >> 32) : 0u);
+#pragma unroll
+    for (int d = 1; d < 8; d <<= 1)
+#pragma unroll
+      for (int k = 0; k < 3; ++k) wd[k] |= shfl_xor(wd[k], d);
+    if (i == 0) {
+      uint32_t* out = reinterpret_cast<uint32_t*>(dst + 12 * (lane >> 3));
+      out[0] = wd[0];
+      out[1] = wd[1];
+      out[2] = wd[2];
+    }
+  }
+  if (lane == 0) a.norms[vec] = ni.n16;
+}
+
+template <int BITS>
+__global__ void __launch_bounds__(64) hlwq_kv_append_small_kernel(const KvAppendArgs a) {
+  const int lane = threadIdx.x;
+  const uint32_t bhi = blockIdx.x;
+  const int64_t total = a.tokens + a.n_new;
+  const int64_t leave_end = total - a.n_res;
+  const int64_t leave_begin = a.tokens > a.n_res ? a.tokens - a.n_res : 0;
+  const uint2* src = reinterpret_cast<const uint2*>(a.src + static_cast<int64_t>(bhi) * a.n_new * kKvDim);
+  // the new tokens that stay in the window: t in [max(tokens, total - n_res), total)
+  const int64_t t0 = leave_end > a.tokens ? leave_end : a.tokens;
+  const int nstay = static_cast<int>(total - t0);
+  uint2 stay[kSmallAppend];
+#pragma unroll
+  for (int k = 0; k < kSmallAppend; ++k)
+    if (k < nstay) stay[k] = src[(t0 + k - a.tokens) * (kKvDim / 4) + lane];
+  for (int64_t o = leave_begin; o < leave_end; ++o) {
+    const uint2* p = o < a.tokens
+                         ? reinterpret_cast<const uint2*>(a.ring + (static_cast<int64_t>(bhi) * a.n_res + o % a.n_res) * kKvDim)
+                         : src + (o - a.tokens) * (kKvDim / 4);
+    append_encode_wave<BITS>(a, bhi, o, p[lane], lane);
+  }
+  // every ring read above has returned before any slot is rewritten
+  wait_vmem();
+  uint2* ring = reinterpret_cast<uint2*>(a.ring + static_cast<int64_t>(bhi) * a.n_res * kKvDim);
+#pragma unroll
+  for (int k = 0; k < kSmallAppend; ++k)
+    if (k < nstay) ring[((t0 + k) % a.n_res) * (kKvDim / 4) + lane] = stay[k];
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -1493,6 +1607,12 @@ int run_kv_append(const void* src, int64_t batch, int64_t heads, int64_t n_new, 
   a.bh = static_cast<uint32_t>(bh);
   a.window_jobs = n_residual > 0 ? static_cast<uint32_t>(bh) : 0u;
   a.in_batches = static_cast<uint32_t>(in_batches);
+  if (n_new <= kSmallAppend) {
+    // latency path: one wave per head
+    if (bits == 3) hipLaunchKernelGGL(hlwq_kv_append_small_kernel<3>, dim3(static_cast<uint32_t>(bh)), dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL(hlwq_kv_append_small_kernel<2>, dim3(static_cast<uint32_t>(bh)), dim3(64), 0, stream, a);
+    return launch_status();
+  }
   const int64_t all_jobs = a.window_jobs + jobs;
   if (all_jobs == 0) return HLWQ_OK;
   const dim3 grid(static_cast<uint32_t>(ceil_div(all_jobs, kWaves))), block(kThreads);
