@@ -328,7 +328,7 @@ def decode_main(args, bits):
     wq.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    step, vectors, nbytes = decode_workload(torch, wq, dev, bits, args.warmup + args.steps)
+    step, vectors, nbytes = decode_workload(torch, wq, dev, bits, args.warmup + 2 * args.steps)
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         step()
@@ -343,6 +343,23 @@ def decode_main(args, bits):
     wall = time.perf_counter() - t0
     ms = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in range(args.steps)])
     ms_per_step = wall * 1e3 / args.steps
+    # the same steps captured in one HIP graph, as a serving loop issues them:
+    # replays repeat the captured appends (same cost, positions and sizes), so
+    # this is a timing of the launches without host overhead
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(args.steps):
+            step()
+    graph.replay()
+    torch.cuda.synchronize()
+    replays = 5
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(replays):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / (replays * args.steps)
     result = {
         "metric": "KV decode-step append: vectors encoded per second (latency-bound)",
         "value": vectors / (ms_per_step * 1e-3),
@@ -360,6 +377,8 @@ def decode_main(args, bits):
                    "vectors_per_step": vectors},
         "append": {"ms": round(float(ms.mean()), 4), "ms_median": round(float(np.median(ms)), 4),
                    "ms_min": round(float(ms.min()), 4), "ms_max": round(float(ms.max()), 4)},
+        "graph": {"ms_per_step": round(graph_ms, 5), "vectors_per_s": vectors / (graph_ms * 1e-3),
+                  "steps_per_graph": args.steps, "replays": replays},
         "roofline": {"bound": "hbm", "kernel": "hlwq_kv_append_small_kernel (one wave per head)", "achieved":
                      round(nbytes / (ms.mean() * 1e-3) / 1e9, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(nbytes / (ms.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS, 6), "traffic": None,

@@ -622,3 +622,56 @@ def test_tq3_qwen36_moe_bank_full(wq):
         assert torch.isfinite(n).all() and (n > 0).all()
     del items, outs
     torch.cuda.empty_cache()
+
+
+def test_kv_decode_steps_in_a_hip_graph(wq):
+    # a decode loop is launch-bound, so callers capture it: 12 appends (single
+    # tokens through the latency path, one 20-token chunk through the batch
+    # kernel) recorded into one graph and replayed three times, each replay
+    # from the same starting state (restored eagerly in between) and each
+    # checked against the same appends run eagerly
+    B, H, T, n_res, bits = 2, 3, 300, 128, 3
+    kv = synth.random_bf16((B, H, T, 256), seed=41, sigma=1.0)
+    chunks = [1] * 6 + [20] + [1] * 5
+    new = synth.random_bf16((B, H, sum(chunks), 256), seed=42, sigma=1.0)
+    cap = T - n_res + sum(chunks)
+    packed0 = torch.full((B, H, cap, 32 * bits), 0xAB, dtype=torch.uint8, device="cuda")
+    norms0 = torch.full((B, H, cap), 7.0, dtype=torch.float16, device="cuda")
+    p0, n0 = wq.hlwq_kv_quantize(to_dev(kv), n_residual=n_res, bits=bits)
+    packed0[:, :, :T - n_res] = p0
+    norms0[:, :, :T - n_res] = n0
+    window0 = torch.empty((B, H, n_res, 256), dtype=torch.bfloat16, device="cuda")
+    dev = to_dev(kv)
+    for t in range(T - n_res, T):
+        window0[:, :, t % n_res] = dev[:, :, t]
+    parts, o = [], 0
+    for n in chunks:
+        parts.append(to_dev(new[:, :, o:o + n]))
+        o += n
+
+    def run(window, packed, norms):
+        tokens = T
+        for part in parts:
+            tokens = wq.hlwq_kv_append(part, window, packed, norms, tokens, n_residual=n_res, bits=bits)
+
+    ew, ep, en = window0.clone(), packed0.clone(), norms0.clone()
+    run(ew, ep, en)
+    torch.cuda.synchronize()
+    gw, gp, gn = window0.clone(), packed0.clone(), norms0.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(gw, gp, gn)
+    for r in range(3):
+        gw.copy_(window0)
+        gp.copy_(packed0)
+        gn.copy_(norms0)
+        torch.cuda.synchronize()
+        _say("kv append graph replay", r)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(gp, ep) and torch.equal(gn, en) and torch.equal(gw, ew), f"replay {r}"
+    # and the eager result is the oracle's
+    op, on, ow = ref.kv_stream_c([kv] + [new[:, :, s:s + n] for s, n in zip(np.cumsum([0] + chunks[:-1]), chunks)],
+                                 n_residual=n_res, bits=bits)
+    assert np.array_equal(ep.cpu().numpy()[:, :, :op.shape[2]], op)
+    assert np.array_equal(f16_bits(en)[:, :, :op.shape[2]], on.view(np.uint16))
