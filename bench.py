@@ -257,10 +257,11 @@ def int4_workload(torch, wq, dev, bits, config="dense_5120", copies=2):
     }
 
 
-def kv_workload(torch, wq, dev, copies=2, n_residual=128, bits=3):
+def kv_workload(torch, wq, dev, copies=3, n_residual=128, bits=3):
     """K and V of the cache held as one tensor [2 * batch, heads, tokens, 256]
-    (K first), so one launch encodes (or decodes) both; two copies, and
-    dequantize reads the copy that quantize did not just write."""
+    (K first), so one launch encodes (or decodes) both; three rotating copies
+    (0.9 GB, well past the 256 MB memory-side cache), and dequantize reads a
+    copy that quantize did not just write."""
     sets = []
     for c in range(copies):
         host = np.concatenate([synth.kv_cache("kv_h256", t, seed=synth.DEFAULT_SEED + c) for t in ("K", "V")], axis=0)
