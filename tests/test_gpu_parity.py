@@ -675,3 +675,31 @@ def test_kv_decode_steps_in_a_hip_graph(wq):
                                  n_residual=n_res, bits=bits)
     assert np.array_equal(ep.cpu().numpy()[:, :, :op.shape[2]], op)
     assert np.array_equal(f16_bits(en)[:, :, :op.shape[2]], on.view(np.uint16))
+
+
+def test_matrix_beyond_4_gib(wq):
+    # one 81920 x 32768 bf16 matrix (5.4 GB): byte offsets past 2^32 in W, the
+    # codes and the output.  Rows repeat a seeded pattern of 61 rows (a prime,
+    # so a row-addressing error of 2^k rows lands on a different pattern row);
+    # sampled rows around the 2^32-byte boundaries and at the end are checked
+    # against the oracle bit for bit
+    rows, n_in, period = 81920, 32768, 61
+    pattern = synth.random_bf16((period, n_in), seed=77, key=3, outlier_frac=0.001, outlier_mult=20.0)
+    pat = to_dev(pattern)
+    w = torch.empty((rows, n_in), dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, rows, period):
+        n = min(period, rows - r0)
+        w[r0:r0 + n] = pat[:n]
+    _say("4 GiB+ matrix filled")
+    packed, norms = wq.hlwq_quantize(w, 5)
+    out = wq.hlwq_dequantize(packed, norms, n_in, 5)
+    torch.cuda.synchronize()
+    boundary = (1 << 31) // n_in  # first row past 2^32 bytes of W
+    for r in (0, 1, boundary - 1, boundary, boundary + 1, 2 * boundary // 2 + 777, rows - 2, rows - 1):
+        src = pattern[r % period][None, :]
+        op, on = ref.quantize_c(src, 5)
+        assert np.array_equal(packed[r].cpu().numpy(), op[0]), r
+        assert np.array_equal(f16_bits(norms[r]), on[0].view(np.uint16)), r
+        assert np.array_equal(bf16_bits(out[r]), ref.dequantize_c(op, on, n_in, 5)[0]), r
+    del w, out, packed, norms
+    torch.cuda.empty_cache()
