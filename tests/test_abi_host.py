@@ -235,3 +235,22 @@ def test_tq3_argument_errors(lib):
     assert lib.hlwq_tq3_quantize_grouped(descs, 1, 42, None) == EALIGN
     assert lib.hlwq_tq3_dequantize_grouped(None, 1, 42, None) == ENULL
     assert lib.hlwq_tq3_quantize_grouped(descs, -1, 42, None) == ESHAPE
+
+
+def test_plain_c_client(tmp_path):
+    # the header compiles as C and a C program can link and call the library
+    import os
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    lib_dir = os.path.dirname(wq.binding.LIB_PATH)
+    exe = str(tmp_path / "c_abi_check")
+    subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(root, "include"),
+                    os.path.join(root, "tests", "c_abi_check.c"), "-L", lib_dir, "-lhlwq",
+                    "-Wl,-rpath," + lib_dir, "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "c abi ok" in r.stdout
