@@ -254,3 +254,22 @@ def test_plain_c_client(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     assert "c abi ok" in r.stdout
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    # the product path has no fallback: without libhlwq.so every call raises
+    monkeypatch.setattr(wq.binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        wq.binding.load_library(str(tmp_path / "libhlwq.so"))
+
+
+def test_binding_rejects_host_tensors():
+    # device memory only: a CPU tensor is refused before any library call
+    import torch
+    w = torch.zeros((4, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device memory"):
+        wq.hlwq_quantize(w, 5)
+    with pytest.raises(ValueError, match="device memory"):
+        wq.hlwq_tq3_quantize(w)
+    with pytest.raises(TypeError):
+        wq.hlwq_quantize(w.float(), 5)
