@@ -703,3 +703,23 @@ def test_matrix_beyond_4_gib(wq):
         assert np.array_equal(bf16_bits(out[r]), ref.dequantize_c(op, on, n_in, 5)[0]), r
     del w, out, packed, norms
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_shapes(wq, case):
+    # seeded random shapes and value scales, every weight entry point on the same matrix
+    from oracle import tq3_ref as tq
+    rng = np.random.default_rng(1000 + case)
+    rows = int(rng.integers(1, 700))
+    n_in = int(rng.choice([int(rng.integers(1, 1200)), 128 * int(rng.integers(1, 12))]))
+    sigma = float(np.exp(rng.uniform(-12, 4)))
+    dist = str(rng.choice(["normal", "student_t5"]))
+    wb = synth.random_bf16((rows, n_in), seed=2000 + case, key=7, dist=dist, sigma=sigma)
+    _say("random shape", case, rows, n_in, f"{sigma:.3g}", dist)
+    for bits in (5, 3):
+        check_matrix(wq, wb, bits, f"random-{case}-q{bits}")
+        codes, norms = wq.hlwq_quantize_codes8(to_dev(wb), bits)
+        torch.cuda.synchronize()
+        oc, on = ref.quantize_codes8_c(wb, bits)
+        assert np.array_equal(codes.cpu().numpy(), oc) and np.array_equal(f16_bits(norms), on.view(np.uint16))
+    check_tq3(wq, wb, 42 if case % 2 == 0 else int(rng.integers(0, 2 ** 63)), f"random-{case}-tq3")
