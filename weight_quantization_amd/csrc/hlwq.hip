@@ -477,31 +477,6 @@ __device__ __forceinline__ int64_t first_lane64(int64_t v) {
   return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// Read one 128-value block whose bytes start at byte offset `off` (a multiple
-// of 16) of a swizzled stage; only the first n values are real.
-__device__ __forceinline__ void read_staged_block(const uint8_t* stage, uint32_t off, int n, float (&x)[kBlock]) {
-  const uint32_t q0 = off >> 4;
-#pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (8 * c < n) v = *reinterpret_cast<const u32x4*>(stage + 16u * swz(q0 + c));
-    unpack8(v, x, c);
-  }
-}
-
-// Write the first n values (n a multiple of 8) of a block, already packed as
-// bf16 pairs, at byte offset `off` of a swizzled stage.
-__device__ __forceinline__ void write_staged_block(uint8_t* stage, uint32_t off, int n, const uint32_t (&pk)[kBlock / 2]) {
-  const uint32_t q0 = off >> 4;
-#pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    if (8 * c < n) {
-      const u32x4 v = {pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]};
-      *reinterpret_cast<u32x4*>(stage + 16u * swz(q0 + c)) = v;
-    }
-  }
-}
-
 // Fast paths for a full batch whose blocks are all whole and contiguous
 // (64 x 256 bytes): lane l's block sits at bytes [256 l, 256 l + 256) of the
 // batch, so its chunk c lives in slot 16 l + (c ^ (l & 15)) and its LDS
@@ -515,6 +490,32 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 }
 __device__ __forceinline__ u32x4 lds_read16(uint32_t a) { return *(const lds_u32x4*)static_cast<uintptr_t>(a); }
 __device__ __forceinline__ void lds_write16(uint32_t a, u32x4 v) { *(lds_u32x4*)static_cast<uintptr_t>(a) = v; }
+
+// Read one 128-value block whose bytes start at byte offset `off` (a multiple
+// of 16) of a swizzled stage; only the first n values are real.  Chunks past
+// n are read from `zero` (the LDS address of 16 zero bytes) instead of being
+// skipped, so every lane runs the same instructions and no chunk needs a
+// branch.
+__device__ __forceinline__ void read_staged_block(const uint8_t* stage, uint32_t off, int n, float (&x)[kBlock],
+                                                  uint32_t zero) {
+  const uint32_t base = lds_addr(stage);
+  const uint32_t q0 = off >> 4;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) unpack8(lds_read16(8 * c < n ? base + 16u * swz(q0 + c) : zero), x, c);
+}
+
+// Write the first n values (n a multiple of 8) of a block, already packed as
+// bf16 pairs, at byte offset `off` of a swizzled stage.  Chunks past n go to
+// `junk` (the LDS address of a 16-byte slot nobody reads).
+__device__ __forceinline__ void write_staged_block(uint8_t* stage, uint32_t off, int n, const uint32_t (&pk)[kBlock / 2],
+                                                   uint32_t junk) {
+  const uint32_t base = lds_addr(stage);
+  const uint32_t q0 = off >> 4;
+#pragma unroll
+  for (int c = 0; c < 16; ++c)
+    lds_write16(8 * c < n ? base + 16u * swz(q0 + c) : junk, u32x4{pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]});
+}
+
 
 // Buffer resource over `bytes` bytes at `base` (raw, unswizzled): the full
 // paths address a batch as base + per-lane VGPR offset + scalar offset, so
@@ -709,10 +710,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   // one LDS array: the entry table at offset 0 (so its reads need no base
   // add), the bucket table, TQ3's pair-square table, then the 256-byte
   // aligned per-wave stages
-  constexpr int kTab = 256 + (TQ ? 2 : 1) * HLWQ_BUCKETS;
+  constexpr int kZero = 256 + (TQ ? 2 : 1) * HLWQ_BUCKETS;  // 16 zero bytes for the reads past a tail block
+  constexpr int kTab = kZero + 256;
   __shared__ __attribute__((aligned(256))) uint8_t lds[kTab + kWaves * kStage];
   uint32_t* tab = reinterpret_cast<uint32_t*>(lds);
   uint8_t* stage_all = lds + kTab;
+  if (threadIdx.x < 4) tab[kZero / 4 + threadIdx.x] = 0u;
   const uint32_t* src_bucket = (BITS == 5) ? c_bucket5 : c_bucket3;
   const uint32_t* src_entry = (BITS == 5) ? c_entry5 : c_entry3;
   for (int i = threadIdx.x; i < HLWQ_BUCKETS / 4; i += kThreads) tab[64 + i] = src_bucket[i];
@@ -760,7 +763,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
         const uint32_t end = __builtin_amdgcn_readlane(off + 2u * p.n, p.nvalid - 1);
         stage_in<16, true, kNt>(reinterpret_cast<const uint8_t*>(g.w[d] + e0), end, stage, lane, sl);
         wait_vmem();
-        read_staged_block(stage, off, p.n, x);
+        read_staged_block(stage, off, p.n, x, lds_addr(lds + kZero));
       } else {
         load_block(g.w[d] + p.e, p.n, x);
       }
@@ -806,8 +809,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   static_assert(!TQ || (BITS == 3 && FIELD == 3), "TQ3 stores packed 3-bit codes");
   // one LDS array: the centroid pair table at offset 0, then the per-wave stages
   constexpr int kPairs = 8 << (2 * BITS);
-  __shared__ __attribute__((aligned(256))) uint8_t lds[kPairs + kWaves * kStage];
-  uint8_t* stage_all = lds + kPairs;
+  constexpr int kJunk = kPairs;  // a 16-byte slot for the writes past a tail block
+  __shared__ __attribute__((aligned(256))) uint8_t lds[kPairs + 256 + kWaves * kStage];
+  uint8_t* stage_all = lds + kPairs + 256;
   fill_pairs<BITS>(reinterpret_cast<float*>(lds), (BITS == 5) ? c_cent5 : c_cent3);
   __syncthreads();
 
@@ -870,7 +874,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       const uint32_t off = static_cast<uint32_t>(p.e - e0) * 2u;
       const uint32_t end = __builtin_amdgcn_readlane(off + 2u * p.n, p.nvalid - 1);
       // lanes past the end of the batch repeat the last block: identical bytes
-      write_staged_block(stage, off, p.n, pk);
+      write_staged_block(stage, off, p.n, pk, lds_addr(lds + kJunk));
       stage_out<16, true>(reinterpret_cast<uint8_t*>(g.w[d] + e0), end, stage, lane, sl);
     } else if (static_cast<uint32_t>(lane) < p.nvalid) {
       store_block(g.w[d] + p.e, p.n, pk);
