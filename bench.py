@@ -445,6 +445,8 @@ def cpu_baseline(config, bits, budget_s=10.0):
     are drawn before each worker's clock starts; only oracle calls are timed."""
     import multiprocessing as mp
     cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    with mp.get_context("fork").Pool(1) as pool:  # one process alone on the host
+        single = pool.map(_oracle_worker, [(config, bits, 0, budget_s / 2)])[0]
     with mp.get_context("fork").Pool(cores) as pool:
         res = pool.map(_oracle_worker, [(config, bits, k, budget_s) for k in range(cores)])
     done = sum(r[0] for r in res)
@@ -456,6 +458,7 @@ def cpu_baseline(config, bits, budget_s=10.0):
         "unit": "weights/s",
         "cores": cores,
         "kind": "oracle",
+        "single_process": {"value": single[0] / single[1], "seconds": round(single[1], 2)},
         "sample": f"{cores} processes x {budget_s:.0f} s, each on {what} of {config} "
                   f"({'TQ3' if config.endswith('_tq3') else f'Q{bits}'} quantize+"
                   f"{'dequantize to INT4' if config == 'dense_5120_int4' else 'dequantize'}, repeated): "
