@@ -76,7 +76,8 @@ enum {
   HLWQ_ERR_BLOCK = -4,   /* block != 128 (weights) or head_dim != 256 (KV) */
   HLWQ_ERR_DEVICE = -5,  /* the HIP launch reported an error */
   HLWQ_ERR_ALIGN = -6,   /* a buffer violates the alignment stated above */
-  HLWQ_ERR_LIMIT = -7    /* more than 2^31 - 1 blocks / vectors in one matrix or cache */
+  HLWQ_ERR_LIMIT = -7    /* more than 2^31 - 1 blocks / vectors in one matrix or cache, or an append
+                            whose launch would exceed 2^32 - 1 work-items (about 6.7e7 heads) */
 };
 
 /* One matrix of a grouped call.  For hlwq_quantize_grouped `w` is read and
@@ -164,8 +165,9 @@ int hlwq_tq3_dequantize_grouped(const hlwq_mat_desc* mats, int n, uint64_t seed,
 /* Quantize several matrices (e.g. the gate_up and down banks of a MoE layer,
  * every expert of which is quantised independently: "Gemma-4-26B-A4B-it-HLWQ-Q5",
  * "Technical Details") in one launch.  `mats` is a host array of n
- * descriptors, read before the call returns; more than 16 descriptors are
- * split over several launches.  bits = 5 or 3, block 128. */
+ * descriptors, read before the call returns; more than 16 descriptors, or
+ * more blocks than one launch addresses (about 8.6e9), are split over several
+ * launches.  bits = 5 or 3, block 128. */
 int hlwq_quantize_grouped(const hlwq_mat_desc* mats, int n, int bits, void* hip_stream);
 
 /* Inverse of hlwq_quantize_grouped over the same descriptors. */

@@ -705,6 +705,34 @@ def test_matrix_beyond_4_gib(wq):
     torch.cuda.empty_cache()
 
 
+def test_kv_cache_split_over_launches(wq):
+    # 67,108,897 heads of one quantised token each (34 GB of bf16): more
+    # 16-token batches than one dequantize grid of 2^24 - 1 workgroups
+    # addresses, so both calls split the cache by heads over two launches.
+    # Heads repeat a seeded pattern of 61 vectors (a prime); sampled heads at
+    # the start, around the split and at the end are checked bit for bit.
+    n_split = 4 * (0xFFFFFFFF // 256)  # batches (here heads) in the first launch
+    H, period = n_split + 37, 61
+    pattern = synth.random_bf16((period, 256), seed=91, sigma=1.0)
+    idx = torch.arange(H, device="cuda") % period
+    dev = to_dev(pattern)[idx].view(1, H, 1, 256)
+    del idx
+    _say("kv split", H)
+    packed, norms = wq.hlwq_kv_quantize(dev, n_residual=0)
+    out = torch.empty_like(dev)
+    wq.hlwq_kv_dequantize(packed, norms, out, n_residual=0)
+    torch.cuda.synchronize()
+    heads = [0, 1, 60, 61, n_split - 2, n_split - 1, n_split, n_split + 1, H - 1]
+    sl = pattern[[h % period for h in heads]].reshape(1, len(heads), 1, 256)
+    op, on = ref.kv_quantize_c(sl, n_residual=0)
+    hs = torch.tensor(heads, device="cuda")
+    assert np.array_equal(packed[0, hs].cpu().numpy(), op[0])
+    assert np.array_equal(f16_bits(norms[0, hs]), on[0].view(np.uint16))
+    assert np.array_equal(bf16_bits(out[0, hs]), ref.kv_dequantize_c(op, on)[0])
+    del dev, out, packed, norms
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("case", range(12))
 def test_random_shapes(wq, case):
     # seeded random shapes and value scales, every weight entry point on the same matrix

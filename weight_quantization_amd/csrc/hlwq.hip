@@ -1011,6 +1011,7 @@ struct KvArgs {
   uint32_t tq;        // quantised tokens per head
   uint32_t nbt;       // batches per head, ceil(tq / 16)
   uint32_t total_batches;
+  uint32_t chunk;      // batches per workgroup, 0 for a persistent grid (batch_range)
 };
 
 constexpr int kKvTokens = 16;    // tokens per batch
@@ -1063,7 +1064,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
   const uint32_t v = ul >> 2;  // token of the batch
   const float sgn1 = pair_sign(q & 1u), sgn2 = pair_sign(q & 2u);
 
-  for (uint32_t b = blockIdx.x * kWaves + wave; b < a.total_batches; b += gridDim.x * kWaves) {
+  const BatchRange br = batch_range(a.total_batches, a.chunk, wave);
+  for (uint32_t b = br.b; b < br.end; b += br.step) {
     asm volatile("" : "+v"(vsrc), "+v"(row_a));  // keep the address bases in one VGPR each
     const KvBatch p = kv_batch(a, b);
     const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv + (static_cast<int64_t>(p.bh) * a.tokens + p.t0) * kKvDim);
@@ -1127,7 +1129,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
   const float sgn1 = pair_sign(q & 1u), sgn2 = pair_sign(q & 2u);
   const SwzLane linear{};
 
-  for (uint32_t b = blockIdx.x * kWaves + wave; b < a.total_batches; b += gridDim.x * kWaves) {
+  const BatchRange br = batch_range(a.total_batches, a.chunk, wave);
+  for (uint32_t b = br.b; b < br.end; b += br.step) {
     asm volatile("" : "+v"(vsrc), "+v"(stage_a));
     const KvBatch p = kv_batch(a, b);
     const uint32_t vv = v < p.nvalid ? v : p.nvalid - 1u;  // lanes past the end repeat the last token
@@ -1426,6 +1429,8 @@ int check_weight_desc(const hlwq_mat_desc& m, int64_t* blocks, int norm_bytes = 
 }
 
 constexpr uint32_t kDequantChunk = 2 * kWaves;  // batches per dequantize workgroup
+// Workgroups per launch: a dispatch's size in work-items is a 32-bit field.
+constexpr int64_t kMaxDispatch = 0xffffffffll / kThreads;
 
 // Resident workgroups per launch: per_cu per CU (the weight kernels use ~200
 // VGPRs and ~68 KB of LDS per workgroup, so two fit; the KV kernels ~110 VGPRs
@@ -1479,6 +1484,8 @@ int run_weight_group(const hlwq_mat_desc* mats, int n, int bits, int field, hipS
       int64_t nblk;
       check_weight_desc(mats[i], &nblk, norm_bytes);
       if (nblk == 0) continue;
+      // a matrix has at most 2^25 batches, so a launch always takes its first one
+      if (batches + ceil_div(nblk, 64) > kDequantChunk * kMaxDispatch) break;
       const int k = g.n++;
       g.batch_start[k] = static_cast<uint32_t>(batches);
       g.nblocks[k] = static_cast<uint32_t>(nblk);
@@ -1490,7 +1497,6 @@ int run_weight_group(const hlwq_mat_desc* mats, int n, int bits, int field, hipS
       g.staged[k] = (mats[i].in % 8 == 0) && ((reinterpret_cast<uintptr_t>(mats[i].w) & 15u) == 0);
       g.whole[k] = g.staged[k] && (mats[i].in % kBlock == 0);
       batches += ceil_div(nblk, 64);
-      if (batches > 0x7fffffff) return HLWQ_ERR_LIMIT;
     }
     if (g.n == 0) continue;
     g.batch_start[g.n] = static_cast<uint32_t>(batches);
@@ -1575,18 +1581,36 @@ int run_kv(bool quant, const void* kv, void* packed, void* norms, int64_t batch,
   a.tokens = tokens;
   a.tq = static_cast<uint32_t>(tq);
   a.nbt = static_cast<uint32_t>(ceil_div(tq, kKvTokens));
-  int64_t batches;
-  if (!mul_ok(bh, a.nbt, &batches) || batches > 0x7fffffff) return HLWQ_ERR_LIMIT;
-  a.total_batches = static_cast<uint32_t>(batches);
-  const dim3 grid(persistent_grid(a.total_batches, 4)), block(kThreads);
-  if (quant) {
-    if (bits == 3) hipLaunchKernelGGL(hlwq_kv_quantize_kernel<3>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(hlwq_kv_quantize_kernel<2>, grid, block, 0, stream, a);
-  } else {
-    if (bits == 3) hipLaunchKernelGGL(hlwq_kv_dequantize_kernel<3>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(hlwq_kv_dequantize_kernel<2>, grid, block, 0, stream, a);
+  // quantize: a persistent grid; dequantize: one batch per wave, workgroups
+  // handed out by the hardware (measured 12-15% faster for the KV dequantizer
+  // on a 2 x 4-head cache of 32768 tokens, 2-5% slower for the quantizer,
+  // whose workgroups first fill 4 KB of search tables)
+  a.chunk = quant ? 0u : static_cast<uint32_t>(kWaves);
+  // one launch takes whole heads, at most kMaxDispatch workgroups' worth of batches
+  const int64_t max_batches = static_cast<int64_t>(kWaves) * kMaxDispatch;
+  if (a.nbt > max_batches) return HLWQ_ERR_LIMIT;
+  const int64_t heads_per_launch = max_batches / a.nbt;
+  const int64_t vec_bytes = 32 * bits;
+  for (int64_t h0 = 0; h0 < bh; h0 += heads_per_launch) {
+    const int64_t nh = bh - h0 < heads_per_launch ? bh - h0 : heads_per_launch;
+    KvArgs l = a;
+    l.kv += h0 * tokens * kKvDim;
+    l.packed += h0 * tq * vec_bytes;
+    l.norms += h0 * tq;
+    l.total_batches = static_cast<uint32_t>(nh * a.nbt);
+    const dim3 grid(quant ? persistent_grid(l.total_batches, 4) : (l.total_batches + l.chunk - 1) / l.chunk),
+        block(kThreads);
+    if (quant) {
+      if (bits == 3) hipLaunchKernelGGL(hlwq_kv_quantize_kernel<3>, grid, block, 0, stream, l);
+      else hipLaunchKernelGGL(hlwq_kv_quantize_kernel<2>, grid, block, 0, stream, l);
+    } else {
+      if (bits == 3) hipLaunchKernelGGL(hlwq_kv_dequantize_kernel<3>, grid, block, 0, stream, l);
+      else hipLaunchKernelGGL(hlwq_kv_dequantize_kernel<2>, grid, block, 0, stream, l);
+    }
+    const int st = launch_status();
+    if (st != HLWQ_OK) return st;
   }
-  return launch_status();
+  return HLWQ_OK;
 }
 
 int run_dequantize_int4(const void* packed, const void* norms, int64_t n_mats, int64_t out, int64_t in, int block,
@@ -1655,12 +1679,14 @@ int run_kv_append(const void* src, int64_t batch, int64_t heads, int64_t n_new, 
   a.in_batches = static_cast<uint32_t>(in_batches);
   if (n_new <= kSmallAppend) {
     // latency path: one wave per head
+    if (bh > kMaxDispatch * kThreads / 64) return HLWQ_ERR_LIMIT;
     if (bits == 3) hipLaunchKernelGGL(hlwq_kv_append_small_kernel<3>, dim3(static_cast<uint32_t>(bh)), dim3(64), 0, stream, a);
     else hipLaunchKernelGGL(hlwq_kv_append_small_kernel<2>, dim3(static_cast<uint32_t>(bh)), dim3(64), 0, stream, a);
     return launch_status();
   }
   const int64_t all_jobs = a.window_jobs + jobs;
   if (all_jobs == 0) return HLWQ_OK;
+  if (ceil_div(all_jobs, kWaves) > kMaxDispatch) return HLWQ_ERR_LIMIT;
   const dim3 grid(static_cast<uint32_t>(ceil_div(all_jobs, kWaves))), block(kThreads);
   if (bits == 3) hipLaunchKernelGGL(hlwq_kv_append_kernel<3>, grid, block, 0, stream, a);
   else hipLaunchKernelGGL(hlwq_kv_append_kernel<2>, grid, block, 0, stream, a);
