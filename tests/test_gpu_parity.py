@@ -677,6 +677,93 @@ def test_kv_decode_steps_in_a_hip_graph(wq):
     assert np.array_equal(f16_bits(en)[:, :, :op.shape[2]], on.view(np.uint16))
 
 
+def test_weight_kernels_in_a_hip_graph(wq):
+    # grouped Q5 quantize + dequantize of two matrices (one with tail blocks)
+    # and a TQ3 quantize + dequantize, captured in one HIP graph and replayed
+    # three times into cleared outputs; every replay must equal the eager
+    # calls, and those the oracle
+    from oracle import tq3_ref as tq
+    wa = synth.random_bf16((300, 1000), seed=31, key=5, outlier_frac=0.001, outlier_mult=20.0)
+    wb = synth.random_bf16((257, 384), seed=32, key=5)
+    ws = [to_dev(wa), to_dev(wb)]
+
+    def buffers():  # allocated outside any capture
+        qs = [wq.hlwq_quantize(w, 5) for w in ws]
+        t = wq.hlwq_tq3_quantize(ws[0])
+        return qs, t, [torch.empty_like(ws[0]), torch.empty_like(ws[1]), torch.empty_like(ws[0])]
+
+    def run(qs, t, outs):
+        wq.hlwq_quantize_grouped([(w, p, n) for w, (p, n) in zip(ws, qs)], 5)
+        wq.hlwq_dequantize_grouped([(o, p, n) for o, (p, n) in zip(outs, qs)], 5)
+        wq.hlwq_tq3_quantize(ws[0], packed=t[0], norms=t[1])
+        wq.hlwq_tq3_dequantize(t[0], t[1], ws[0].shape[1], out=outs[2])
+
+    def clear(qs, t, outs):
+        for x in [v for pn in qs for v in pn] + list(t) + outs:
+            x.zero_()
+
+    eq, et, eo = buffers()
+    clear(eq, et, eo)
+    run(eq, et, eo)
+    torch.cuda.synchronize()
+    gq, gt, go = buffers()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(gq, gt, go)
+    for r in range(3):
+        clear(gq, gt, go)
+        torch.cuda.synchronize()
+        _say("weight graph replay", r)
+        graph.replay()
+        torch.cuda.synchronize()
+        for (a, b), (c, d) in zip(gq, eq):
+            assert torch.equal(a, c) and torch.equal(b, d), f"replay {r}: codes / norms"
+        assert torch.equal(gt[0], et[0]) and torch.equal(gt[1], et[1]), f"replay {r}: TQ3"
+        assert all(torch.equal(a, b) for a, b in zip(go, eo)), f"replay {r}: dequantized"
+    for w_bits, (p, n), o in zip((wa, wb), eq, eo):
+        op, on = ref.quantize_c(w_bits, 5)
+        assert np.array_equal(p.cpu().numpy(), op) and np.array_equal(f16_bits(n), on.view(np.uint16))
+        assert np.array_equal(bf16_bits(o), ref.dequantize_c(op, on, w_bits.shape[1], 5))
+    tp, tn = tq.quantize_c(wa)
+    assert np.array_equal(et[0].cpu().numpy(), tp) and np.array_equal(f32_bits(et[1]), tn.view(np.uint32))
+    assert np.array_equal(bf16_bits(eo[2]), tq.dequantize_c(tp, tn, wa.shape[1]))
+
+
+def test_concurrent_calls_from_threads(wq):
+    # four host threads, each with its own stream and matrix, call quantize and
+    # dequantize at the same time (the library keeps no per-call state; its one
+    # lazily filled value, the CU count, is an atomic); all results are the
+    # oracle's
+    import threading
+    mats = [synth.random_bf16((200 + 37 * k, 640 + 64 * k), seed=40 + k, key=5) for k in range(4)]
+    devs = [to_dev(m) for m in mats]
+    torch.cuda.synchronize()
+    results, errors = [None] * 4, []
+
+    def work(k):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(5):
+                    p, n = wq.hlwq_quantize(devs[k], 5)
+                    o = wq.hlwq_dequantize(p, n, mats[k].shape[1], 5)
+            s.synchronize()
+            results[k] = (p, n, o)
+        except Exception as e:  # reported below, in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for m, (p, n, o) in zip(mats, results):
+        op, on = ref.quantize_c(m, 5)
+        assert np.array_equal(p.cpu().numpy(), op) and np.array_equal(f16_bits(n), on.view(np.uint16))
+        assert np.array_equal(bf16_bits(o), ref.dequantize_c(op, on, m.shape[1], 5))
+
+
 def test_matrix_beyond_4_gib(wq):
     # one 81920 x 32768 bf16 matrix (5.4 GB): byte offsets past 2^32 in W, the
     # codes and the output.  Rows repeat a seeded pattern of 61 rows (a prime,
