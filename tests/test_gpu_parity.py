@@ -171,6 +171,23 @@ def test_grouped_launch_splits(wq):
         assert np.array_equal(bf16_bits(o), ref.dequantize_c(op, on, wb.shape[1], 5))
 
 
+def test_binding_rejects_another_device(wq, monkeypatch):
+    # the library launches on the current device, so tensors or a stream of
+    # another device are refused before any call (one GPU here: the other
+    # device is faked)
+    w = to_dev(synth.random_bf16((4, 256), seed=3))
+
+    class OtherStream:
+        device_index = torch.cuda.current_device() + 1
+        cuda_stream = 0
+
+    with pytest.raises(ValueError, match="current device"):
+        wq.hlwq_quantize(w, 5, stream=OtherStream())
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: w.device.index + 1)
+    with pytest.raises(ValueError, match="current device"):
+        wq.hlwq_quantize(w, 5)
+
+
 def test_non_default_stream_and_determinism(wq):
     wb = synth.random_bf16((512, 2048), seed=12)
     w = to_dev(wb)

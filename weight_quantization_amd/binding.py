@@ -164,8 +164,12 @@ def _torch():
 
 
 def _stream_handle(stream=None) -> int:
+    # the library launches on the current device: an explicit stream must be its
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream()
+    cur = torch.cuda.current_device()
+    if s.device_index != cur:
+        raise ValueError(f"stream is on cuda:{s.device_index}, the current device is cuda:{cur}")
     return int(s.cuda_stream)
 
 
@@ -181,6 +185,10 @@ def _need(t, dtype, name):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be in device memory")
+    cur = torch.cuda.current_device()
+    if t.device.index != cur:
+        raise ValueError(f"{name} is on {t.device}, the current device is cuda:{cur}; "
+                         f"call under torch.cuda.device({t.device.index})")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
