@@ -176,10 +176,11 @@ def test_kv_append_argument_errors(lib):
     assert ap(A, 1, 4, 1, 500, A, 128, A + 8, A, 400, 256, 3, None) == EALIGN
     assert ap(A, 1, 4, 1, 500, A, 128, A, A + 1, 400, 256, 2, None) == EALIGN
     # a launch of more than 2^32 - 1 work-items: one 64-lane wave per head
-    # (decode path), or one wave per head plus one per 32 tokens that arrive
-    # and leave in the same call
+    # (decode path), or one wave per head for the ring of a longer append
     assert ap(A, 1, 2 ** 26, 1, 500, A, 128, A, A, 400, 256, 3, None) == ELIMIT
-    assert ap(A, 1, 2 ** 24, 200, 500, A, 128, A, A, 600, 256, 3, None) == ELIMIT
+    assert ap(A, 1, 2 ** 26, 200, 500, A, 128, A, A, 600, 256, 3, None) == ELIMIT
+    # more than 2^31 - 1 tokens of one head arriving and leaving in one call
+    assert ap(A, 1, 1, 2 ** 31 + 200, 0, A, 128, A, A, 2 ** 31 + 72, 256, 3, None) == ELIMIT
     # nothing to append, or nobody to append to
     assert ap(None, 1, 4, 0, 500, None, 128, None, None, 0, 256, 3, None) == OK
     assert ap(None, 0, 4, 3, 500, None, 128, None, None, 0, 256, 3, None) == OK

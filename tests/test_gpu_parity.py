@@ -176,16 +176,17 @@ def test_binding_rejects_another_device(wq, monkeypatch):
     # another device are refused before any call (one GPU here: the other
     # device is faked)
     w = to_dev(synth.random_bf16((4, 256), seed=3))
+    other = w.device.index + 1
 
     class OtherStream:
-        device_index = torch.cuda.current_device() + 1
+        device_index = other
         cuda_stream = 0
 
-    with pytest.raises(ValueError, match="current device"):
+    with pytest.raises(ValueError, match="stream is on"):
         wq.hlwq_quantize(w, 5, stream=OtherStream())
-    monkeypatch.setattr(torch.cuda, "current_device", lambda: w.device.index + 1)
-    with pytest.raises(ValueError, match="current device"):
-        wq.hlwq_quantize(w, 5)
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: other)
+    with pytest.raises(ValueError, match="a tensor is on"):
+        wq.hlwq_quantize(w, 5, stream=OtherStream())
 
 
 def test_non_default_stream_and_determinism(wq):

@@ -163,13 +163,18 @@ def _torch():
     return torch
 
 
-def _stream_handle(stream=None) -> int:
-    # the library launches on the current device: an explicit stream must be its
+def _stream_handle(stream=None, *tensors) -> int:
+    """The stream to launch on.  The library launches on the current device,
+    so the stream and every tensor of the call must be on it."""
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream()
     cur = torch.cuda.current_device()
     if s.device_index != cur:
         raise ValueError(f"stream is on cuda:{s.device_index}, the current device is cuda:{cur}")
+    for t in tensors:
+        if t is not None and t.get_device() != cur:
+            raise ValueError(f"a tensor is on cuda:{t.get_device()}, the current device is cuda:{cur}; "
+                             f"call under torch.cuda.device({t.get_device()})")
     return int(s.cuda_stream)
 
 
@@ -185,10 +190,6 @@ def _need(t, dtype, name):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be in device memory")
-    cur = torch.cuda.current_device()
-    if t.device.index != cur:
-        raise ValueError(f"{name} is on {t.device}, the current device is cuda:{cur}; "
-                         f"call under torch.cuda.device({t.device.index})")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
@@ -216,7 +217,7 @@ def hlwq_quantize(w, bits: int = 5, packed=None, norms=None, stream=None):
     if tuple(packed.shape) != pshape or tuple(norms.shape) != nshape:
         raise ValueError("packed / norms shape mismatch")
     st = load_library().hlwq_quantize(_ptr(w), n_mats, out, n_in, BLOCK, bits, _ptr(packed), _ptr(norms),
-                                      _stream_handle(stream))
+                                      _stream_handle(stream, w, packed, norms))
     _check("hlwq_quantize", st)
     return packed, norms
 
@@ -239,7 +240,7 @@ def hlwq_dequantize(packed, norms, n_in: int, bits: int = 5, out=None, stream=No
     if tuple(out.shape) != lead + (n_in,):
         raise ValueError("out shape mismatch")
     st = load_library().hlwq_dequantize(_ptr(packed), _ptr(norms), n_mats, rows, n_in, BLOCK, bits, _ptr(out),
-                                        _stream_handle(stream))
+                                        _stream_handle(stream, packed, norms, out))
     _check("hlwq_dequantize", st)
     return out
 
@@ -259,7 +260,7 @@ def hlwq_quantize_codes8(w, bits: int = 5, codes=None, norms=None, stream=None):
     if tuple(codes.shape) != pshape or tuple(norms.shape) != nshape:
         raise ValueError("codes / norms shape mismatch")
     st = load_library().hlwq_quantize_codes8(_ptr(w), n_mats, out, n_in, BLOCK, bits, _ptr(codes), _ptr(norms),
-                                             _stream_handle(stream))
+                                             _stream_handle(stream, w, codes, norms))
     _check("hlwq_quantize_codes8", st)
     return codes, norms
 
@@ -281,7 +282,7 @@ def hlwq_dequantize_codes8(codes, norms, n_in: int, bits: int = 5, out=None, str
     if tuple(out.shape) != lead + (n_in,):
         raise ValueError("out shape mismatch")
     st = load_library().hlwq_dequantize_codes8(_ptr(codes), _ptr(norms), n_mats, rows, n_in, BLOCK, bits, _ptr(out),
-                                               _stream_handle(stream))
+                                               _stream_handle(stream, codes, norms, out))
     _check("hlwq_dequantize_codes8", st)
     return out
 
@@ -301,7 +302,7 @@ def hlwq_tq3_quantize(w, seed: int = TQ3_SEED, packed=None, norms=None, stream=N
     if tuple(packed.shape) != pshape or tuple(norms.shape) != nshape:
         raise ValueError("packed / norms shape mismatch")
     st = load_library().hlwq_tq3_quantize(_ptr(w), n_mats, out, n_in, BLOCK, seed & (2 ** 64 - 1), _ptr(packed),
-                                          _ptr(norms), _stream_handle(stream))
+                                          _ptr(norms), _stream_handle(stream, w, packed, norms))
     _check("hlwq_tq3_quantize", st)
     return packed, norms
 
@@ -323,7 +324,8 @@ def hlwq_tq3_dequantize(packed, norms, n_in: int, seed: int = TQ3_SEED, out=None
     if tuple(out.shape) != lead + (n_in,):
         raise ValueError("out shape mismatch")
     st = load_library().hlwq_tq3_dequantize(_ptr(packed), _ptr(norms), n_mats, rows, n_in, BLOCK,
-                                            seed & (2 ** 64 - 1), _ptr(out), _stream_handle(stream))
+                                            seed & (2 ** 64 - 1), _ptr(out),
+                                            _stream_handle(stream, packed, norms, out))
     _check("hlwq_tq3_dequantize", st)
     return out
 
@@ -355,7 +357,8 @@ def hlwq_dequantize_int4(packed, norms, n_in: int, bits: int = 5, q4=None, scale
             tuple(zeros.shape) != lead + (nb,):
         raise ValueError("q4 / scales / zeros shape mismatch")
     st = load_library().hlwq_dequantize_int4(_ptr(packed), _ptr(norms), n_mats, rows, n_in, BLOCK, bits, _ptr(q4),
-                                             _ptr(scales), _ptr(zeros), _stream_handle(stream))
+                                             _ptr(scales), _ptr(zeros),
+                                             _stream_handle(stream, packed, norms, q4, scales, zeros))
     _check("hlwq_dequantize_int4", st)
     return q4, scales, zeros
 
@@ -380,7 +383,8 @@ def hlwq_quantize_grouped(items, bits: int = 5, stream=None):
         if tuple(p.shape) != ps or tuple(n.shape) != ns:
             raise ValueError("packed / norms shape mismatch")
     arr = _descs(items)
-    st = load_library().hlwq_quantize_grouped(arr, len(items), bits, _stream_handle(stream))
+    st = load_library().hlwq_quantize_grouped(arr, len(items), bits,
+                                              _stream_handle(stream, *[t for item in items for t in item]))
     _check("hlwq_quantize_grouped", st)
 
 
@@ -395,7 +399,8 @@ def hlwq_dequantize_grouped(items, bits: int = 5, stream=None):
         if tuple(p.shape) != ps or tuple(n.shape) != ns:
             raise ValueError("packed / norms shape mismatch")
     arr = _descs(items)
-    st = load_library().hlwq_dequantize_grouped(arr, len(items), bits, _stream_handle(stream))
+    st = load_library().hlwq_dequantize_grouped(arr, len(items), bits,
+                                                _stream_handle(stream, *[t for item in items for t in item]))
     _check("hlwq_dequantize_grouped", st)
 
 
@@ -414,7 +419,7 @@ def hlwq_tq3_quantize_grouped(items, seed: int = TQ3_SEED, stream=None):
     """items: list of (w bf16, packed u8, norms fp32) triples, all preallocated."""
     _check_tq3_items(items)
     st = load_library().hlwq_tq3_quantize_grouped(_descs(items), len(items), seed & (2 ** 64 - 1),
-                                                  _stream_handle(stream))
+                                                  _stream_handle(stream, *[t for item in items for t in item]))
     _check("hlwq_tq3_quantize_grouped", st)
 
 
@@ -422,7 +427,7 @@ def hlwq_tq3_dequantize_grouped(items, seed: int = TQ3_SEED, stream=None):
     """items: list of (w_out bf16, packed u8, norms fp32) triples, all preallocated."""
     _check_tq3_items(items)
     st = load_library().hlwq_tq3_dequantize_grouped(_descs(items), len(items), seed & (2 ** 64 - 1),
-                                                    _stream_handle(stream))
+                                                    _stream_handle(stream, *[t for item in items for t in item]))
     _check("hlwq_tq3_dequantize_grouped", st)
 
 
@@ -444,7 +449,7 @@ def hlwq_kv_quantize(kv, n_residual: int = 128, bits: int = 3, packed=None, norm
     if tuple(packed.shape) != (B, H, tq, D * bits // 8) or tuple(norms.shape) != (B, H, tq):
         raise ValueError("packed / norms shape mismatch")
     st = load_library().hlwq_kv_quantize(_ptr(kv), B, H, T, D, bits, n_residual, _ptr(packed), _ptr(norms),
-                                         _stream_handle(stream))
+                                         _stream_handle(stream, kv, packed, norms))
     _check("hlwq_kv_quantize", st)
     return packed, norms
 
@@ -471,7 +476,7 @@ def hlwq_kv_append(new_kv, window, packed, norms, tokens: int, n_residual: int =
         raise ValueError("packed / norms shape mismatch")
     st = load_library().hlwq_kv_append(_ptr(new_kv), B, H, n_new, tokens, _ptr(window) if window is not None else None,
                                        n_residual, _ptr(packed), _ptr(norms), capacity, D, bits,
-                                       _stream_handle(stream))
+                                       _stream_handle(stream, new_kv, window, packed, norms))
     _check("hlwq_kv_append", st)
     return tokens + n_new
 
@@ -487,6 +492,6 @@ def hlwq_kv_dequantize(packed, norms, kv_out, n_residual: int = 128, bits: int =
     if tuple(packed.shape) != (B, H, tq, D * bits // 8) or tuple(norms.shape) != (B, H, tq):
         raise ValueError("packed / norms shape mismatch")
     st = load_library().hlwq_kv_dequantize(_ptr(packed), _ptr(norms), B, H, T, D, bits, n_residual, _ptr(kv_out),
-                                           _stream_handle(stream))
+                                           _stream_handle(stream, packed, norms, kv_out))
     _check("hlwq_kv_dequantize", st)
     return kv_out

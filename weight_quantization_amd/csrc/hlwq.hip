@@ -1005,9 +1005,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 
 struct KvArgs {
   uint16_t* kv;       // [bh][tokens][256]
-  uint8_t* packed;    // [bh][tq][32 * bits]
-  uint16_t* norms;    // [bh][tq]
-  int64_t tokens;
+  uint8_t* packed;    // [bh][out_stride][32 * bits]
+  uint16_t* norms;    // [bh][out_stride]
+  int64_t tokens;     // kv rows per head
+  int64_t out_stride; // packed / norms rows per head
+  int64_t out_offset; // row of token 0 in packed / norms
   uint32_t tq;        // quantised tokens per head
   uint32_t nbt;       // batches per head, ceil(tq / 16)
   uint32_t total_batches;
@@ -1103,7 +1105,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     } else {
       *reinterpret_cast<u32x4*>(stage + 16u * ul) = u32x4{words[0], words[1], words[2], words[3]};
     }
-    const size_t vec0 = static_cast<size_t>(p.bh) * a.tq + p.t0;
+    const size_t vec0 = static_cast<size_t>(p.bh) * a.out_stride + a.out_offset + p.t0;
     const SwzLane linear{};
     stage_out<2, false>(a.packed + vec0 * kVec, p.nvalid * kVec, stage, lane, linear);
     if (q == 0u && v < p.nvalid) a.norms[vec0 + v] = ni.n16;
@@ -1134,7 +1136,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     asm volatile("" : "+v"(vsrc), "+v"(stage_a));
     const KvBatch p = kv_batch(a, b);
     const uint32_t vv = v < p.nvalid ? v : p.nvalid - 1u;  // lanes past the end repeat the last token
-    const size_t vec0 = static_cast<size_t>(p.bh) * a.tq + p.t0;
+    const size_t vec0 = static_cast<size_t>(p.bh) * a.out_stride + a.out_offset + p.t0;
     stage_in<2, false, 0>(a.packed + vec0 * kVec, p.nvalid * kVec, stage, lane, linear);
     const float scale = f16_value(a.norms[vec0 + vv]) * 0x1p-8f;
     wait_vmem();
@@ -1189,11 +1191,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
 // Streaming KV append: during generation every new token enters the bf16
 // window of the newest n_residual tokens (a ring: token t in slot
 // t mod n_residual), and the token it pushes out is encoded into the packed
-// cache.  One wave per job: job h < bh is head h's "window job" (encode the
-// leaving tokens that are still in the ring, then write the new tokens that
-// stay into the ring, in that order, so no slot is overwritten before it is
-// read); the other jobs encode, 32 at a time, leaving tokens that arrive and
-// leave within this call (read from the new tokens directly).
+// cache.  The new tokens that arrive and leave within one call are encoded
+// straight from the new tokens by the KV quantize kernel (launch_kv with the
+// cache's row stride and the call's first row).  The ring is handled by one
+// wave per head: it encodes the leaving tokens that are still in the ring,
+// then writes the new tokens that stay into the ring, in that order, so no
+// slot is overwritten before it is read.
 // ---------------------------------------------------------------------------
 
 struct KvAppendArgs {
@@ -1203,8 +1206,6 @@ struct KvAppendArgs {
   uint16_t* norms;      // [bh][capacity]
   int64_t tokens, n_new, n_res, capacity;
   uint32_t bh;           // batch * heads
-  uint32_t window_jobs;  // bh if n_res > 0, else 0
-  uint32_t in_batches;   // per head: ceil(max(n_new - n_res, 0) / 32)
 };
 
 // Encode tokens o0 .. o0 + count - 1 (count <= 32) of head bhi: lane pair
@@ -1212,13 +1213,12 @@ struct KvAppendArgs {
 // store nothing), each lane one half of its 256 values.
 template <int BITS>
 __device__ __forceinline__ void append_encode(const KvAppendArgs& a, const uint8_t* __restrict__ lds, uint32_t bhi,
-                                              int64_t o0, uint32_t count, bool from_ring, int lane) {
+                                              int64_t o0, uint32_t count, int lane) {
   constexpr uint32_t kVec = 32 * BITS;
   const uint32_t v = static_cast<uint32_t>(lane) >> 1;
   const uint32_t half = lane & 1;
   const int64_t o = o0 + (v < count ? v : count - 1);
-  const uint16_t* p = from_ring ? a.ring + (static_cast<int64_t>(bhi) * a.n_res + o % a.n_res) * kKvDim
-                                : a.src + (static_cast<int64_t>(bhi) * a.n_new + (o - a.tokens)) * kKvDim;
+  const uint16_t* p = a.ring + (static_cast<int64_t>(bhi) * a.n_res + o % a.n_res) * kKvDim;
   float x[kBlock];
   load_block(p + half * kBlock, kBlock, x);
   const float s_half = sumsq_tree(x);
@@ -1245,28 +1245,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
-  const uint32_t job = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t bhi = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (bhi >= a.bh) return;
   const int64_t total = a.tokens + a.n_new;
-  const int64_t leave_end = total - a.n_res;  // tokens below this index are encoded afterwards
-  uint32_t bhi;
-  int64_t o_begin, o_end;
-  const bool window_job = job < a.window_jobs;
-  if (window_job) {
-    bhi = job;
-    o_begin = a.tokens > a.n_res ? a.tokens - a.n_res : 0;  // oldest token in the ring
-    o_end = leave_end < a.tokens ? leave_end : a.tokens;     // leaving tokens still in the ring
-  } else {
-    const uint32_t j = job - a.window_jobs;
-    if (j >= a.bh * a.in_batches) return;
-    bhi = j / a.in_batches;
-    o_begin = a.tokens + 32 * static_cast<int64_t>(j - bhi * a.in_batches);
-    o_end = o_begin + 32 < leave_end ? o_begin + 32 : leave_end;
-  }
+  const int64_t leave_end = total - a.n_res;                          // tokens below this index are encoded afterwards
+  const int64_t o_begin = a.tokens > a.n_res ? a.tokens - a.n_res : 0;  // oldest token in the ring
+  const int64_t o_end = leave_end < a.tokens ? leave_end : a.tokens;     // leaving tokens still in the ring
   for (int64_t o0 = o_begin; o0 < o_end; o0 += 32) {
     const int64_t n = o_end - o0;
-    append_encode<BITS>(a, lds, bhi, o0, static_cast<uint32_t>(n < 32 ? n : 32), window_job, lane);
+    append_encode<BITS>(a, lds, bhi, o0, static_cast<uint32_t>(n < 32 ? n : 32), lane);
   }
-  if (!window_job) return;
   // every ring read above has returned before any slot is rewritten
   wait_vmem();
   // the new tokens that stay in the window: t in [max(tokens, total - n_res), total)
@@ -1558,6 +1546,42 @@ int make_single(const void* w, const void* packed, const void* norms, int64_t n_
   return HLWQ_OK;
 }
 
+// Launch the KV quantize or dequantize kernel over bh heads of `a` (a.tq
+// tokens each, a.tokens kv rows and a.out_stride packed rows per head), whole
+// heads per launch, at most kMaxDispatch workgroups' worth of batches each.
+int launch_kv(bool quant, int bits, KvArgs a, int64_t bh, hipStream_t stream) {
+  a.nbt = static_cast<uint32_t>(ceil_div(a.tq, kKvTokens));
+  // quantize: a persistent grid; dequantize: one batch per wave, workgroups
+  // handed out by the hardware (measured 12-15% faster for the KV dequantizer
+  // on a 2 x 4-head cache of 32768 tokens, 2-5% slower for the quantizer,
+  // whose workgroups first fill 4 KB of search tables)
+  a.chunk = quant ? 0u : static_cast<uint32_t>(kWaves);
+  const int64_t max_batches = static_cast<int64_t>(kWaves) * kMaxDispatch;
+  if (a.nbt > max_batches) return HLWQ_ERR_LIMIT;
+  const int64_t heads_per_launch = max_batches / a.nbt;
+  const int64_t vec_bytes = 32 * bits;
+  for (int64_t h0 = 0; h0 < bh; h0 += heads_per_launch) {
+    const int64_t nh = bh - h0 < heads_per_launch ? bh - h0 : heads_per_launch;
+    KvArgs l = a;
+    l.kv += h0 * a.tokens * kKvDim;
+    l.packed += h0 * a.out_stride * vec_bytes;
+    l.norms += h0 * a.out_stride;
+    l.total_batches = static_cast<uint32_t>(nh * a.nbt);
+    const dim3 grid(quant ? persistent_grid(l.total_batches, 4) : (l.total_batches + l.chunk - 1) / l.chunk),
+        block(kThreads);
+    if (quant) {
+      if (bits == 3) hipLaunchKernelGGL(hlwq_kv_quantize_kernel<3>, grid, block, 0, stream, l);
+      else hipLaunchKernelGGL(hlwq_kv_quantize_kernel<2>, grid, block, 0, stream, l);
+    } else {
+      if (bits == 3) hipLaunchKernelGGL(hlwq_kv_dequantize_kernel<3>, grid, block, 0, stream, l);
+      else hipLaunchKernelGGL(hlwq_kv_dequantize_kernel<2>, grid, block, 0, stream, l);
+    }
+    const int st = launch_status();
+    if (st != HLWQ_OK) return st;
+  }
+  return HLWQ_OK;
+}
+
 int run_kv(bool quant, const void* kv, void* packed, void* norms, int64_t batch, int64_t heads, int64_t tokens,
            int head_dim, int bits, int64_t n_residual, hipStream_t stream) {
   if (head_dim != kKvDim) return HLWQ_ERR_BLOCK;
@@ -1579,38 +1603,10 @@ int run_kv(bool quant, const void* kv, void* packed, void* norms, int64_t batch,
   a.packed = static_cast<uint8_t*>(packed);
   a.norms = static_cast<uint16_t*>(norms);
   a.tokens = tokens;
+  a.out_stride = tq;
+  a.out_offset = 0;
   a.tq = static_cast<uint32_t>(tq);
-  a.nbt = static_cast<uint32_t>(ceil_div(tq, kKvTokens));
-  // quantize: a persistent grid; dequantize: one batch per wave, workgroups
-  // handed out by the hardware (measured 12-15% faster for the KV dequantizer
-  // on a 2 x 4-head cache of 32768 tokens, 2-5% slower for the quantizer,
-  // whose workgroups first fill 4 KB of search tables)
-  a.chunk = quant ? 0u : static_cast<uint32_t>(kWaves);
-  // one launch takes whole heads, at most kMaxDispatch workgroups' worth of batches
-  const int64_t max_batches = static_cast<int64_t>(kWaves) * kMaxDispatch;
-  if (a.nbt > max_batches) return HLWQ_ERR_LIMIT;
-  const int64_t heads_per_launch = max_batches / a.nbt;
-  const int64_t vec_bytes = 32 * bits;
-  for (int64_t h0 = 0; h0 < bh; h0 += heads_per_launch) {
-    const int64_t nh = bh - h0 < heads_per_launch ? bh - h0 : heads_per_launch;
-    KvArgs l = a;
-    l.kv += h0 * tokens * kKvDim;
-    l.packed += h0 * tq * vec_bytes;
-    l.norms += h0 * tq;
-    l.total_batches = static_cast<uint32_t>(nh * a.nbt);
-    const dim3 grid(quant ? persistent_grid(l.total_batches, 4) : (l.total_batches + l.chunk - 1) / l.chunk),
-        block(kThreads);
-    if (quant) {
-      if (bits == 3) hipLaunchKernelGGL(hlwq_kv_quantize_kernel<3>, grid, block, 0, stream, l);
-      else hipLaunchKernelGGL(hlwq_kv_quantize_kernel<2>, grid, block, 0, stream, l);
-    } else {
-      if (bits == 3) hipLaunchKernelGGL(hlwq_kv_dequantize_kernel<3>, grid, block, 0, stream, l);
-      else hipLaunchKernelGGL(hlwq_kv_dequantize_kernel<2>, grid, block, 0, stream, l);
-    }
-    const int st = launch_status();
-    if (st != HLWQ_OK) return st;
-  }
-  return HLWQ_OK;
+  return launch_kv(quant, bits, a, bh, stream);
 }
 
 int run_dequantize_int4(const void* packed, const void* norms, int64_t n_mats, int64_t out, int64_t in, int block,
@@ -1661,10 +1657,9 @@ int run_kv_append(const void* src, int64_t batch, int64_t heads, int64_t n_new, 
   if ((reinterpret_cast<uintptr_t>(src) & 15u) || (reinterpret_cast<uintptr_t>(ring) & 15u) ||
       (reinterpret_cast<uintptr_t>(packed) & 15u) || (reinterpret_cast<uintptr_t>(norms) & 1u))
     return HLWQ_ERR_ALIGN;
+  // new tokens that arrive and leave within this call: rows tokens .. tokens + in_leaving - 1
   const int64_t in_leaving = n_new > n_residual ? n_new - n_residual : 0;
-  const int64_t in_batches = ceil_div(in_leaving, 32);
-  int64_t jobs;
-  if (bh > 0x3fffffff || !mul_ok(bh, in_batches, &jobs) || jobs > 0x3fffffff) return HLWQ_ERR_LIMIT;
+  if (bh > 0x3fffffff || in_leaving > 0x7fffffff) return HLWQ_ERR_LIMIT;
   KvAppendArgs a;
   a.src = static_cast<const uint16_t*>(src);
   a.ring = static_cast<uint16_t*>(ring);
@@ -1675,8 +1670,6 @@ int run_kv_append(const void* src, int64_t batch, int64_t heads, int64_t n_new, 
   a.n_res = n_residual;
   a.capacity = capacity;
   a.bh = static_cast<uint32_t>(bh);
-  a.window_jobs = n_residual > 0 ? static_cast<uint32_t>(bh) : 0u;
-  a.in_batches = static_cast<uint32_t>(in_batches);
   if (n_new <= kSmallAppend) {
     // latency path: one wave per head
     if (bh > kMaxDispatch * kThreads / 64) return HLWQ_ERR_LIMIT;
@@ -1684,10 +1677,27 @@ int run_kv_append(const void* src, int64_t batch, int64_t heads, int64_t n_new, 
     else hipLaunchKernelGGL(hlwq_kv_append_small_kernel<2>, dim3(static_cast<uint32_t>(bh)), dim3(64), 0, stream, a);
     return launch_status();
   }
-  const int64_t all_jobs = a.window_jobs + jobs;
-  if (all_jobs == 0) return HLWQ_OK;
-  if (ceil_div(all_jobs, kWaves) > kMaxDispatch) return HLWQ_ERR_LIMIT;
-  const dim3 grid(static_cast<uint32_t>(ceil_div(all_jobs, kWaves))), block(kThreads);
+  // everything is checked before the first launch
+  if (ceil_div(bh, kWaves) > kMaxDispatch ||
+      ceil_div(in_leaving, kKvTokens) > static_cast<int64_t>(kWaves) * kMaxDispatch)
+    return HLWQ_ERR_LIMIT;
+  if (in_leaving > 0) {
+    // the streaming path's bulk (a prefill, say): the KV quantize kernel,
+    // reading the new tokens and writing cache rows tokens .. leave_end - 1
+    KvArgs k;
+    k.kv = const_cast<uint16_t*>(a.src);
+    k.packed = a.packed;
+    k.norms = a.norms;
+    k.tokens = n_new;
+    k.out_stride = capacity;
+    k.out_offset = tokens;
+    k.tq = static_cast<uint32_t>(in_leaving);
+    const int st = launch_kv(true, bits, k, bh, stream);
+    if (st != HLWQ_OK) return st;
+  }
+  if (n_residual == 0) return HLWQ_OK;
+  // the ring: one wave per head
+  const dim3 grid(static_cast<uint32_t>(ceil_div(bh, kWaves))), block(kThreads);
   if (bits == 3) hipLaunchKernelGGL(hlwq_kv_append_kernel<3>, grid, block, 0, stream, a);
   else hipLaunchKernelGGL(hlwq_kv_append_kernel<2>, grid, block, 0, stream, a);
   return launch_status();
