@@ -168,13 +168,14 @@ def _stream_handle(stream=None, *tensors) -> int:
     so the stream and every tensor of the call must be on it."""
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream()
-    cur = torch.cuda.current_device()
-    if s.device_index != cur:
-        raise ValueError(f"stream is on cuda:{s.device_index}, the current device is cuda:{cur}")
-    for t in tensors:
-        if t is not None and t.get_device() != cur:
-            raise ValueError(f"a tensor is on cuda:{t.get_device()}, the current device is cuda:{cur}; "
-                             f"call under torch.cuda.device({t.get_device()})")
+    if torch.cuda.device_count() > 1 or stream is not None:  # with one device nothing else can be current
+        cur = torch.cuda.current_device()
+        if s.device_index != cur:
+            raise ValueError(f"stream is on cuda:{s.device_index}, the current device is cuda:{cur}")
+        for t in tensors:
+            if t is not None and t.get_device() != cur:
+                raise ValueError(f"a tensor is on cuda:{t.get_device()}, the current device is cuda:{cur}; "
+                                 f"call under torch.cuda.device({t.get_device()})")
     return int(s.cuda_stream)
 
 
