@@ -486,6 +486,39 @@ def test_kv_decode_full(wq, bits):
         assert np.array_equal(w[:, :, t % 128], want), t
 
 
+@pytest.mark.parametrize("bits", [3, 2])
+def test_kv_prefill_append_full(wq, bits):
+    # the whole K + V prompt [2, 4, 32768, 256] appended to an empty streaming
+    # cache in one call, the tokens that leave the window in two calls split
+    # mid-batch, and the static quantization of the same cache (itself checked
+    # against the oracle): identical codes and norms, and the ring holds the
+    # newest 128 tokens
+    kv = np.concatenate([synth.kv_cache("kv_h256", t) for t in ("K", "V")], axis=0)
+    B, H, T, D = kv.shape
+    _say("kv prefill append", bits)
+    dev = to_dev(kv)
+    p0, n0 = wq.hlwq_kv_quantize(dev, n_residual=128, bits=bits)
+    for split in (T, 12345):
+        window = torch.zeros((B, H, 128, D), dtype=torch.bfloat16, device="cuda")
+        packed = torch.zeros((B, H, T, 32 * bits), dtype=torch.uint8, device="cuda")
+        norms = torch.zeros((B, H, T), dtype=torch.float16, device="cuda")
+        tokens = wq.hlwq_kv_append(dev[:, :, :split].contiguous(), window, packed, norms, 0, bits=bits)
+        if split < T:
+            tokens = wq.hlwq_kv_append(dev[:, :, split:].contiguous(), window, packed, norms, tokens, bits=bits)
+        torch.cuda.synchronize()
+        assert tokens == T
+        assert torch.equal(packed[:, :, :T - 128], p0) and torch.equal(norms[:, :, :T - 128], n0), split
+        assert not packed[:, :, T - 128:].any() and not norms[:, :, T - 128:].any(), "rows past the encoded tokens"
+        w = bf16_bits(window)
+        for t in (T - 128, T - 127, T - 2, T - 1):
+            assert np.array_equal(w[:, :, t % 128], kv[:, :, t]), t
+    sl = kv[1:2, 3:4, 20000:20512]
+    op, on = ref.kv_quantize_c(np.concatenate([sl, np.zeros((1, 1, 128, 256), np.uint16)], axis=2),
+                               n_residual=128, bits=bits)
+    assert np.array_equal(p0[1:2, 3:4, 20000:20512].cpu().numpy(), op)
+    assert np.array_equal(f16_bits(n0[1:2, 3:4, 20000:20512]), on.view(np.uint16))
+
+
 # --------------------------------------------------------------------------
 # tolerances against the fp64 definition tier
 # --------------------------------------------------------------------------
