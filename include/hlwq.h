@@ -40,15 +40,18 @@
  *
  * Ownership and execution: the caller allocates every buffer, in device
  * memory of the current HIP device.  The library keeps no state beyond
- * constant tables compiled into the code object and allocates nothing.  Every
+ * constant tables compiled into the code object and each device's compute-unit
+ * count (read once, kept in an atomic), and allocates nothing.  Every
  * call validates its arguments on the host first; on success it enqueues the
  * work on `hip_stream` (a hipStream_t; NULL means the default stream) and
  * returns without synchronising.  Calls are reentrant; calls on different
  * streams may run concurrently.
  *
  * Errors: every int-returning call returns HLWQ_OK (0) or a negative
- * HLWQ_ERR_* status; nothing is enqueued on error and output buffers are left
- * untouched.  Zero-sized work (n_mats, out, in, batch, heads or the quantised
+ * HLWQ_ERR_* status.  On an argument error nothing is enqueued and output
+ * buffers are left untouched; HLWQ_ERR_DEVICE (a launch the runtime refused)
+ * can come after earlier launches of the same call, whose outputs are then
+ * partly written.  Zero-sized work (n_mats, out, in, batch, heads or the quantised
  * token count equal to 0) is valid, does nothing and accepts NULL pointers.
  * Inputs must be finite; a block whose squared norm overflows fp32 (an entry
  * above ~1.8e19 in magnitude) yields an infinite norm and unspecified codes.
