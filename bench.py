@@ -12,10 +12,11 @@ Infinity Cache, so every step streams from HBM.
 Other workloads (--config) use the same procedure: the Gemma-4-26B-A4B-shaped
 bank, the dense hidden-5120 Linears (Q5 or --bits 3; dense_5120_int4 follows
 the quantize with the fused dequantize -> INT4), the H256 KV cache (Q3 or
---bits 2; two independent caches alternate so the working set exceeds the
-cache), the streaming KV decode step (kv_h256_decode, latency-bound), and TQ3 on
-the Qwen3.6-shaped bank (qwen36_moe_bank_tq3).  --layout codes8 stores one code
-per byte.
+--bits 2; three independent caches rotate so the working set exceeds the
+cache), the whole prompt appended to an empty streaming cache in one call
+(kv_h256_prefill), the streaming KV decode step (kv_h256_decode,
+latency-bound), and TQ3 on the Qwen3.6-shaped bank (qwen36_moe_bank_tq3).
+--layout codes8 stores one code per byte.
 
 Prints one JSON line: weights/s of quantize + dequantize, with the per-kernel
 HBM roofline (algorithmic bytes / kernel time from HIP events on the launch
@@ -60,6 +61,10 @@ DESCRIPTIONS = {
                             "quantize+dequantize of gate_up [256,1024,2048] + down [256,2048,512] bf16, "
                             "N(0,0.02^2) with 0.1% x20 outliers: random-sign H128 (seed 42), 8 Lloyd-Max "
                             "centroids, 3-bit codes, fp32 shape-gain norms"),
+    "kv_h256_prefill": ("streaming KV cache K and V [1,4,32768,256] bf16 N(0,1) with a 128-token bf16 window: "
+                        "the whole 32768-token prompt appended to empty caches in one hlwq_kv_append call "
+                        "(KV quantize kernel for the tokens that leave the window, a copy into the ring for the rest), "
+                        "then dequantized"),
     "kv_h256_decode": ("streaming KV cache K and V [1,4,32768,256] bf16 N(0,1) with a 128-token bf16 window: "
                        "one decode step appends one token to each of the 8 head caches (one launch), encoding "
                        "the 8 tokens that leave the window (latency-bound)"),
@@ -295,6 +300,51 @@ def kv_workload(torch, wq, dev, copies=3, n_residual=128, bits=3):
     }
 
 
+def prefill_workload(torch, wq, dev, copies=3, n_residual=128, bits=3):
+    """The K and V prompts ([2, 4, 32768, 256]) appended to empty streaming
+    caches in one hlwq_kv_append call each step, then the encoded tokens
+    dequantized; three rotating sets, as for kv_h256."""
+    sets = []
+    B, H, T, D = synth.CONFIGS["kv_h256"]["K"][1]
+    cap = T - n_residual
+    for c in range(copies):
+        host = np.concatenate([synth.kv_cache("kv_h256", t, seed=synth.DEFAULT_SEED + c) for t in ("K", "V")], axis=0)
+        kv = to_device(torch, dev, host)
+        window = torch.empty((2 * B, H, n_residual, D), dtype=torch.bfloat16, device=dev)
+        p = torch.empty((2 * B, H, cap, 32 * bits), dtype=torch.uint8, device=dev)
+        n = torch.empty((2 * B, H, cap), dtype=torch.float16, device=dev)
+        wq.hlwq_kv_append(kv, window, p, n, 0, n_residual=n_residual, bits=bits)
+        sets.append((kv, window, p, n, kv.clone()))
+    state = {"i": 0}
+    elems = 2 * B * H * T * D
+
+    def append():
+        kv, window, p, n, _ = sets[state["i"] % copies]
+        wq.hlwq_kv_append(kv, window, p, n, 0, n_residual=n_residual, bits=bits)
+
+    def dequant():
+        _, _, p, n, out = sets[(state["i"] + 1) % copies]
+        wq.hlwq_kv_dequantize(p, n, out, n_residual=n_residual, bits=bits)
+        state["i"] += 1
+
+    vec_out = 2 * B * H * cap * (32 * bits + 2)
+    return {
+        "quantize": append,
+        "dequantize": dequant,
+        "weights": elems,
+        # the prompt in; codes and norms of the tokens that leave, and the window, out
+        "bytes": elems * 2 + vec_out + 2 * B * H * n_residual * D * 2,
+        # codes and norms in, bf16 of the encoded tokens out
+        "bytes_d": vec_out + 2 * B * H * cap * D * 2,
+        "kernels": ("hlwq_kv_append (hlwq_kv_quantize_kernel, then hlwq_kv_ring_fill_kernel for the window)",
+                    "hlwq_kv_dequantize_kernel"),
+        "launches": 2,
+        "launches_d": 1,
+        "copies": copies,
+        "keep": sets,
+    }
+
+
 def decode_workload(torch, wq, dev, bits, steps_total, n_residual=128, pool=64):
     """K and V caches (stacked, [2, 4, ...]) prefilled with 32768 tokens; each
     step appends one token per head through hlwq_kv_append."""
@@ -392,7 +442,7 @@ def decode_main(args, bits):
 def _oracle_samples(config, bits, worker):
     """Inputs for one CPU worker: one expert matrix (or 256 rows) of every
     tensor of the workload, or 1024 tokens of one KV head."""
-    if config == "kv_h256":
+    if config in ("kv_h256", "kv_h256_prefill"):
         kv = synth.kv_cache("kv_h256", "K", tokens=1024 + 128)
         return [kv[:, worker % kv.shape[1]:][:, :1]]
     source = {"dense_5120_int4": "dense_5120", "qwen36_moe_bank_tq3": "qwen36_moe_bank"}.get(config, config)
@@ -419,9 +469,13 @@ def _oracle_worker(args):
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
         for w in samples:
-            if config == "kv_h256":
-                p, n = ref.kv_quantize_c(w, n_residual=128)
-                ref.kv_dequantize_c(p, n)
+            if config == "kv_h256_prefill":
+                p, n, _ = ref.kv_stream_c([w], n_residual=128, bits=bits)
+                ref.kv_dequantize_c(p, n, bits=bits)
+                done += p.shape[2] * 256
+            elif config == "kv_h256":
+                p, n = ref.kv_quantize_c(w, n_residual=128, bits=bits)
+                ref.kv_dequantize_c(p, n, bits=bits)
                 done += p.shape[2] * 256
             elif config == "qwen36_moe_bank_tq3":
                 packed, g = tq3_ref.quantize_c(w, 42)
@@ -451,7 +505,7 @@ def cpu_baseline(config, bits, budget_s=10.0):
         res = pool.map(_oracle_worker, [(config, bits, k, budget_s) for k in range(cores)])
     done = sum(r[0] for r in res)
     wall = max(r[1] for r in res)
-    what = ("1024 tokens of one KV head" if config == "kv_h256"
+    what = ("1024 tokens of one KV head" if config in ("kv_h256", "kv_h256_prefill")
             else "one expert matrix (or 256 rows) of each tensor")
     return {
         "value": done / wall,
@@ -512,6 +566,8 @@ def main():
     print(f"[bench] generating {config}", file=sys.stderr, flush=True)
     if config == "kv_h256":
         wl = kv_workload(torch, wq, dev, bits=bits)
+    elif config == "kv_h256_prefill":
+        wl = prefill_workload(torch, wq, dev, bits=bits)
     elif config == "dense_5120_int4":
         wl = int4_workload(torch, wq, dev, bits)
     else:
@@ -577,7 +633,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": DESCRIPTIONS[config], "name": config, "weights": weights, "bits": bits,
-                   "block": 256 if config == "kv_h256" else 128, "input_sets": wl["copies"],
+                   "block": 256 if config.startswith("kv_") else 128, "input_sets": wl["copies"],
                    "layout": "packed" if config.startswith("kv_") else args.layout},
         "hbm_gbs": round(step_gbs, 1),
         "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),

@@ -1193,10 +1193,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
 // t mod n_residual), and the token it pushes out is encoded into the packed
 // cache.  The new tokens that arrive and leave within one call are encoded
 // straight from the new tokens by the KV quantize kernel (launch_kv with the
-// cache's row stride and the call's first row).  The ring is handled by one
-// wave per head: it encodes the leaving tokens that are still in the ring,
-// then writes the new tokens that stay into the ring, in that order, so no
-// slot is overwritten before it is read.
+// cache's row stride and the call's first row).  The leaving tokens that are
+// still in the ring are encoded by one wave per head; a copy kernel launched
+// after it on the same stream then writes the new tokens that stay into their
+// ring slots, so no slot is overwritten before it is read.
 // ---------------------------------------------------------------------------
 
 struct KvAppendArgs {
@@ -1247,25 +1247,31 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
   const int lane = threadIdx.x & 63;
   const uint32_t bhi = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (bhi >= a.bh) return;
-  const int64_t total = a.tokens + a.n_new;
-  const int64_t leave_end = total - a.n_res;                          // tokens below this index are encoded afterwards
+  const int64_t leave_end = a.tokens + a.n_new - a.n_res;              // tokens below this index are encoded afterwards
   const int64_t o_begin = a.tokens > a.n_res ? a.tokens - a.n_res : 0;  // oldest token in the ring
   const int64_t o_end = leave_end < a.tokens ? leave_end : a.tokens;     // leaving tokens still in the ring
   for (int64_t o0 = o_begin; o0 < o_end; o0 += 32) {
     const int64_t n = o_end - o0;
     append_encode<BITS>(a, lds, bhi, o0, static_cast<uint32_t>(n < 32 ? n : 32), lane);
   }
-  // every ring read above has returned before any slot is rewritten
-  wait_vmem();
-  // the new tokens that stay in the window: t in [max(tokens, total - n_res), total)
-  const int64_t t0 = leave_end > a.tokens ? leave_end : a.tokens;
-  const int64_t chunks = (total - t0) * (kKvDim / 8);  // 16-byte chunks
-  for (int64_t c = lane; c < chunks; c += 64) {
-    const int64_t t = t0 + c / (kKvDim / 8);
-    const int64_t k = c % (kKvDim / 8);
-    const u32x4 val = reinterpret_cast<const u32x4*>(a.src + (static_cast<int64_t>(bhi) * a.n_new + (t - a.tokens)) * kKvDim)[k];
-    reinterpret_cast<u32x4*>(a.ring + (static_cast<int64_t>(bhi) * a.n_res + t % a.n_res) * kKvDim)[k] = val;
-  }
+}
+
+// The new tokens that stay in the window, t0 + i for i < ntok (ntok <= n_res),
+// into their ring slots (slot0 + i) mod n_res, one 16-byte chunk per
+// work-item.  Launched after the ring kernel on the same stream, so every ring
+// read of the call has returned before a slot is rewritten.
+__global__ void __launch_bounds__(kThreads) hlwq_kv_ring_fill_kernel(const KvAppendArgs a, int64_t t0, int64_t ntok,
+                                                                     int64_t slot0) {
+  constexpr int64_t kChunks = kKvDim / 8;  // 16-byte chunks per token
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t per_head = ntok * kChunks;
+  if (c >= static_cast<int64_t>(a.bh) * per_head) return;
+  const int64_t h = c / per_head;
+  const int64_t r = c - h * per_head;
+  const int64_t i = r / kChunks, k = r % kChunks;
+  const int64_t slot = slot0 + i < a.n_res ? slot0 + i : slot0 + i - a.n_res;
+  const u32x4 v = reinterpret_cast<const u32x4*>(a.src + (h * a.n_new + (t0 - a.tokens) + i) * kKvDim)[k];
+  reinterpret_cast<u32x4*>(a.ring + (h * a.n_res + slot) * kKvDim)[k] = v;
 }
 
 // Streaming KV append, latency path for a few new tokens per head (a decode
@@ -1678,7 +1684,9 @@ int run_kv_append(const void* src, int64_t batch, int64_t heads, int64_t n_new, 
     return launch_status();
   }
   // everything is checked before the first launch
-  if (ceil_div(bh, kWaves) > kMaxDispatch ||
+  const int64_t staying = n_new < n_residual ? n_new : n_residual;  // new tokens that stay in the window
+  const int64_t fill_groups = ceil_div(bh * staying * (kKvDim / 8), kThreads);
+  if (ceil_div(bh, kWaves) > kMaxDispatch || fill_groups > kMaxDispatch ||
       ceil_div(in_leaving, kKvTokens) > static_cast<int64_t>(kWaves) * kMaxDispatch)
     return HLWQ_ERR_LIMIT;
   if (in_leaving > 0) {
@@ -1696,10 +1704,19 @@ int run_kv_append(const void* src, int64_t batch, int64_t heads, int64_t n_new, 
     if (st != HLWQ_OK) return st;
   }
   if (n_residual == 0) return HLWQ_OK;
-  // the ring: one wave per head
-  const dim3 grid(static_cast<uint32_t>(ceil_div(bh, kWaves))), block(kThreads);
-  if (bits == 3) hipLaunchKernelGGL(hlwq_kv_append_kernel<3>, grid, block, 0, stream, a);
-  else hipLaunchKernelGGL(hlwq_kv_append_kernel<2>, grid, block, 0, stream, a);
+  if (leave_begin < (leave_end < tokens ? leave_end : tokens)) {
+    // ring tokens leave: one wave per head encodes them
+    const dim3 grid(static_cast<uint32_t>(ceil_div(bh, kWaves))), block(kThreads);
+    if (bits == 3) hipLaunchKernelGGL(hlwq_kv_append_kernel<3>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(hlwq_kv_append_kernel<2>, grid, block, 0, stream, a);
+    const int st = launch_status();
+    if (st != HLWQ_OK) return st;
+  }
+  // then the new tokens that stay are written into the ring
+  const int64_t t0 = leave_end > tokens ? leave_end : tokens;
+  const int64_t ntok = total - t0;
+  hipLaunchKernelGGL(hlwq_kv_ring_fill_kernel, dim3(static_cast<uint32_t>(fill_groups)), dim3(kThreads), 0, stream, a,
+                     t0, ntok, t0 % n_residual);
   return launch_status();
 }
 
