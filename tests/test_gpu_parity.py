@@ -279,6 +279,44 @@ def test_kv_append_matches_token_stream(wq, bits, chunks, n_res):
     _append_case(wq, 2, 3, chunks, n_res, bits, seed=len(chunks) * 10 + n_res + bits)
 
 
+@pytest.mark.parametrize("case", range(12))
+def test_kv_random_shapes(wq, case):
+    # seeded random cache shapes, residual windows, value scales and bit
+    # widths through quantize and dequantize
+    rng = np.random.default_rng(3000 + case)
+    B, H, T = int(rng.integers(1, 4)), int(rng.integers(1, 6)), int(rng.integers(1, 700))
+    n_res = int(rng.choice([0, 1, 7, 128, 200]))
+    bits = int(rng.choice([3, 2]))
+    sigma = float(np.exp(rng.uniform(-12, 4)))
+    kv = synth.random_bf16((B, H, T, 256), seed=4000 + case, key=9, sigma=sigma)
+    _say("kv random", case, (B, H, T), "n_res", n_res, "bits", bits, f"{sigma:.3g}")
+    dev = to_dev(kv)
+    packed, norms = wq.hlwq_kv_quantize(dev, n_residual=n_res, bits=bits)
+    out = to_dev(np.full((B, H, T, 256), 0x3F80, np.uint16))
+    wq.hlwq_kv_dequantize(packed, norms, out, n_residual=n_res, bits=bits)
+    torch.cuda.synchronize()
+    op, on = ref.kv_quantize_c(kv, n_residual=n_res, bits=bits)
+    assert np.array_equal(packed.cpu().numpy(), op)
+    assert np.array_equal(f16_bits(norms), on.view(np.uint16))
+    tq = max(T - n_res, 0)
+    got = bf16_bits(out)
+    assert np.array_equal(got[:, :, :tq], ref.kv_dequantize_c(op, on, bits=bits))
+    assert np.all(got[:, :, tq:] == 0x3F80)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_kv_append_random_chunkings(wq, case):
+    # seeded random chunkings (single tokens, decode-sized and prefill-sized
+    # chunks mixed) and windows through the streaming append
+    rng = np.random.default_rng(5000 + case)
+    n_res = int(rng.choice([1, 5, 32, 128]))
+    sizes = [1, 2, 8, 9, 16, 33, 100, 300]
+    chunks = tuple(int(rng.choice(sizes)) for _ in range(int(rng.integers(2, 9))))
+    bits = int(rng.choice([3, 2]))
+    _say("kv append random", case, chunks, "n_res", n_res, "bits", bits)
+    _append_case(wq, int(rng.integers(1, 3)), int(rng.integers(1, 4)), chunks, n_res, bits, seed=6000 + case)
+
+
 def test_kv_cache_underflow_vectors(wq):
     f = synth.f32_to_bf16_bits
     kv = synth.random_bf16((1, 2, 200, 256), seed=77, sigma=1.0)
