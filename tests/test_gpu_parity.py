@@ -926,4 +926,12 @@ def test_random_shapes(wq, case):
         torch.cuda.synchronize()
         oc, on = ref.quantize_codes8_c(wb, bits)
         assert np.array_equal(codes.cpu().numpy(), oc) and np.array_equal(f16_bits(norms), on.view(np.uint16))
+        if n_in % 128 == 0:  # the INT4 groups are the HLWQ blocks
+            packed, n16 = wq.hlwq_quantize(to_dev(wb), bits)
+            q4, scales, zeros = wq.hlwq_dequantize_int4(packed, n16, n_in, bits)
+            torch.cuda.synchronize()
+            op, on = ref.quantize_c(wb, bits)
+            p4, s4, z4 = ref.dequantize_to_int4_c(op, on, n_in, bits)
+            assert np.array_equal(q4.cpu().numpy(), p4) and np.array_equal(zeros.cpu().numpy(), z4)
+            assert np.array_equal(scales.cpu().numpy().view(np.uint32), s4.view(np.uint32))
     check_tq3(wq, wb, 42 if case % 2 == 0 else int(rng.integers(0, 2 ** 63)), f"random-{case}-tq3")
