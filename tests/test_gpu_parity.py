@@ -714,14 +714,15 @@ def test_tq3_qwen36_moe_bank_full(wq):
 
 
 def test_kv_decode_steps_in_a_hip_graph(wq):
-    # a decode loop is launch-bound, so callers capture it: 12 appends (single
-    # tokens through the latency path, one 20-token chunk through the batch
-    # kernel) recorded into one graph and replayed three times, each replay
-    # from the same starting state (restored eagerly in between) and each
-    # checked against the same appends run eagerly
+    # a decode loop is launch-bound, so callers capture it: 14 appends (single
+    # tokens through the latency path, a 20-token chunk through the ring
+    # kernels, a 200-token chunk through the KV quantize kernel as well)
+    # recorded into one graph and replayed three times, each replay from the
+    # same starting state (restored eagerly in between) and each checked
+    # against the same appends run eagerly
     B, H, T, n_res, bits = 2, 3, 300, 128, 3
     kv = synth.random_bf16((B, H, T, 256), seed=41, sigma=1.0)
-    chunks = [1] * 6 + [20] + [1] * 5
+    chunks = [1] * 6 + [20] + [1] * 5 + [200, 1]
     new = synth.random_bf16((B, H, sum(chunks), 256), seed=42, sigma=1.0)
     cap = T - n_res + sum(chunks)
     packed0 = torch.full((B, H, cap, 32 * bits), 0xAB, dtype=torch.uint8, device="cuda")
