@@ -171,6 +171,34 @@ def test_grouped_launch_splits(wq):
         assert np.array_equal(bf16_bits(o), ref.dequantize_c(op, on, wb.shape[1], 5))
 
 
+@pytest.mark.parametrize("bits", [5, 3])
+def test_grouped_launch_mixed_paths(wq, bits):
+    # one grouped launch whose matrices take every read path: whole aligned
+    # blocks, aligned rows with a tail block, rows not 16-byte aligned (odd
+    # column counts) and empty matrices, which the launch skips
+    shapes = [(300, 512), (0, 256), (77, 37), (129, 704), (5, 0), (64, 129), (1, 1), (200, 1000)]
+    items, host = [], []
+    for i, (rows, n_in) in enumerate(shapes):
+        wb = synth.random_bf16((rows, n_in), seed=700 + i, key=11, outlier_frac=0.01, outlier_mult=20.0)
+        nb = -(-n_in // 128)
+        items.append((to_dev(wb) if wb.size else torch.empty((rows, n_in), dtype=torch.bfloat16, device="cuda"),
+                      torch.empty((rows, nb, 16 * bits), dtype=torch.uint8, device="cuda"),
+                      torch.empty((rows, nb), dtype=torch.float16, device="cuda")))
+        host.append(wb)
+    _say("grouped mixed paths", bits)
+    wq.hlwq_quantize_grouped(items, bits)
+    outs = [(torch.empty_like(w), p, n) for (w, p, n) in items]
+    wq.hlwq_dequantize_grouped(outs, bits)
+    torch.cuda.synchronize()
+    for (w, p, n), (o, _, _), wb in zip(items, outs, host):
+        if wb.size == 0:
+            continue
+        op, on = ref.quantize_c(wb, bits)
+        assert np.array_equal(p.cpu().numpy(), op), wb.shape
+        assert np.array_equal(f16_bits(n), on.view(np.uint16)), wb.shape
+        assert np.array_equal(bf16_bits(o), ref.dequantize_c(op, on, wb.shape[1], bits)), wb.shape
+
+
 def test_binding_rejects_another_device(wq, monkeypatch):
     # the library launches on the current device, so tensors or a stream of
     # another device are refused before any call (one GPU here: the other
