@@ -9,9 +9,11 @@
 // Work mapping.  One work-item owns one whole 128-block: its 128 values live in
 // VGPRs, so the norm tree, all 7 butterfly stages, the code search and the bit
 // packing are lane-local, and the square root and reciprocal are paid once per
-// 128 weights.  A KV head vector (256 values) is split over two adjacent lanes;
-// only the last norm level and the last butterfly stage (stride 128) cross
-// lanes, through a DPP quad permutation.
+// 128 weights.  A KV head vector (256 values) is split over four adjacent
+// lanes of 64 values: the last two norm levels and the last two butterfly
+// stages (strides 64 and 128) cross lanes through DPP quad permutations (the
+// decode-step append kernel uses four values per lane instead, and the ring
+// append kernel lane pairs).
 //
 // Code search.  A rotated value y becomes, by one fused multiply-add with a
 // denormal addend, a denormal whose bit pattern is the index of its 1/8-wide
@@ -24,8 +26,10 @@
 // Rounding.  The file is compiled with -ffp-contract=off: every + and * below
 // is one IEEE round-to-nearest operation in the order written, sqrtf and the
 // division are correctly rounded, and the only fused multiply-adds are the
-// explicit __builtin_fmaf calls of the first norm-tree level, so no rounding
-// differs from the operation order documented in include/hlwq.h.
+// explicit __builtin_fmaf calls of the first norm-tree level and the
+// cross-lane KV butterflies, a + (+-1) b (the product is exact, so the one
+// rounding is that of a +- b), so no rounding differs from the operation order
+// documented in include/hlwq.h.
 
 #include <hip/hip_runtime.h>
 
@@ -43,6 +47,8 @@ constexpr int kBlock = 128;    // weights per HLWQ block
 constexpr int kKvDim = 256;    // KV head vector length
 constexpr int kThreads = 256;  // work-items per workgroup (4 wave64)
 constexpr int kMaxGroup = 16;  // matrices per grouped launch
+constexpr int kKvPoolWaves = 16;   // waves of the KV quantizer's work-pool workgroup (one per CU)
+constexpr int kKvPoolThreads = 64 * kKvPoolWaves;
 constexpr int kPoolWaves = 8;   // waves of a work-pool workgroup (one workgroup per CU)
 constexpr int kPoolThreads = 64 * kPoolWaves;
 
@@ -1040,6 +1046,42 @@ __device__ __forceinline__ float lane_xor2(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
 }
 
+
+// One butterfly stage across lanes folded into one instruction per value:
+// x = fma(partner's x, c, x) with c = +1 or -1 per lane, v_fmac_f32 with a DPP
+// quad permutation on the partner operand.  The lower lane of a pair gets
+// a + b and the upper one b - a = -(a - b): the true value times a sign the
+// caller tracks (negation is exact, and so is c * partner).  The compiler does
+// not fold a DPP operand into a fused multiply-add, hence the inline assembly;
+// a DPP read of a VGPR needs two wait states after the VALU write of it, which
+// the leading s_nop 1 provides for the whole group (every instruction of a
+// group reads a value written before the group).
+#define HLWQ_FMAC_DPP(i, perm) "v_fmac_f32_dpp %" #i ", %" #i ", %16 quad_perm:" perm " row_mask:0xf bank_mask:0xf\n\t"
+#define HLWQ_FMAC_DPP16(perm)                                                                                          \
+  "s_nop 1\n\t" HLWQ_FMAC_DPP(0, perm) HLWQ_FMAC_DPP(1, perm) HLWQ_FMAC_DPP(2, perm) HLWQ_FMAC_DPP(3, perm)            \
+      HLWQ_FMAC_DPP(4, perm) HLWQ_FMAC_DPP(5, perm) HLWQ_FMAC_DPP(6, perm) HLWQ_FMAC_DPP(7, perm)                      \
+          HLWQ_FMAC_DPP(8, perm) HLWQ_FMAC_DPP(9, perm) HLWQ_FMAC_DPP(10, perm) HLWQ_FMAC_DPP(11, perm)                \
+              HLWQ_FMAC_DPP(12, perm) HLWQ_FMAC_DPP(13, perm) HLWQ_FMAC_DPP(14, perm) HLWQ_FMAC_DPP(15, perm)
+
+template <int XOR>
+__device__ __forceinline__ void cross_stage(float (&x)[64], float c) {
+#pragma unroll
+  for (int j = 0; j < 64; j += 16) {
+    if constexpr (XOR == 1)
+      asm volatile(HLWQ_FMAC_DPP16("[1,0,3,2]")
+                   : "+v"(x[j]), "+v"(x[j + 1]), "+v"(x[j + 2]), "+v"(x[j + 3]), "+v"(x[j + 4]), "+v"(x[j + 5]),
+                     "+v"(x[j + 6]), "+v"(x[j + 7]), "+v"(x[j + 8]), "+v"(x[j + 9]), "+v"(x[j + 10]), "+v"(x[j + 11]),
+                     "+v"(x[j + 12]), "+v"(x[j + 13]), "+v"(x[j + 14]), "+v"(x[j + 15])
+                   : "v"(c));
+    else
+      asm volatile(HLWQ_FMAC_DPP16("[2,3,0,1]")
+                   : "+v"(x[j]), "+v"(x[j + 1]), "+v"(x[j + 2]), "+v"(x[j + 3]), "+v"(x[j + 4]), "+v"(x[j + 5]),
+                     "+v"(x[j + 6]), "+v"(x[j + 7]), "+v"(x[j + 8]), "+v"(x[j + 9]), "+v"(x[j + 10]), "+v"(x[j + 11]),
+                     "+v"(x[j + 12]), "+v"(x[j + 13]), "+v"(x[j + 14]), "+v"(x[j + 15])
+                   : "v"(c));
+  }
+}
+
 struct KvBatch {
   uint32_t bh, t0, nvalid;
 };
@@ -1052,22 +1094,24 @@ __device__ __forceinline__ KvBatch kv_batch(const KvArgs& a, uint32_t b) {
   return p;
 }
 
-template <int BITS>
+template <int BITS, int NT = kThreads>
 __device__ __forceinline__ void fill_kv_search(uint32_t* tab) {
   const uint32_t* bucket = (BITS == 3) ? c_kvbucket3 : c_kvbucket2;
   const uint32_t* entry = (BITS == 3) ? c_entry3 : c_entry2;
-  for (int i = threadIdx.x; i < HLWQ_KV_BUCKETS / 4; i += kThreads) tab[64 + i] = bucket[i];
+  for (int i = threadIdx.x; i < HLWQ_KV_BUCKETS / 4; i += NT) tab[64 + i] = bucket[i];
   if (threadIdx.x < 2 * (1 << BITS)) tab[threadIdx.x] = entry[threadIdx.x];
 }
 
 template <int BITS>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) hlwq_kv_quantize_kernel(const KvArgs a) {
+__global__ void __launch_bounds__(kKvPoolThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) hlwq_kv_quantize_kernel(const KvArgs a) {
   // entry table at offset 0, bucket table, per-wave stages
   constexpr int kTab = 256 + HLWQ_KV_BUCKETS;
   constexpr uint32_t kVec = 32 * BITS;  // packed bytes per vector
-  __shared__ __attribute__((aligned(256))) uint8_t lds[kTab + kWaves * kKvStage];
+  __shared__ __attribute__((aligned(256))) uint8_t lds[kTab + kKvPoolWaves * kKvStage];
+  __shared__ uint32_t next_batch;
+  if (threadIdx.x == 0) next_batch = kKvPoolWaves;
   uint32_t* tab = reinterpret_cast<uint32_t*>(lds);
-  fill_kv_search<BITS>(tab);
+  fill_kv_search<BITS, kKvPoolThreads>(tab);
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -1080,8 +1124,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
   const uint32_t v = ul >> 2;  // token of the batch
   const float sgn1 = pair_sign(q & 1u), sgn2 = pair_sign(q & 2u);
 
-  const BatchRange br = batch_range(a.total_batches, a.chunk, wave);
-  for (uint32_t b = br.b; b < br.end; b += br.step) {
+  // work pool, as in the weight quantizer: one 16-wave workgroup per CU takes
+  // batches blockIdx.x + gridDim.x m in turn from an LDS counter
+  uint32_t m = wave;
+  for (uint32_t b = blockIdx.x + gridDim.x * m; b < a.total_batches;) {
+    uint32_t m_next = 0;
+    if (lane == 0) m_next = __hip_atomic_fetch_add(&next_batch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     asm volatile("" : "+v"(vsrc), "+v"(row_a));  // keep the address bases in one VGPR each
     const KvBatch p = kv_batch(a, b);
     const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv + (static_cast<int64_t>(p.bh) * a.tokens + p.t0) * kKvDim);
@@ -1103,12 +1151,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     const NormInfo ni = norm_info(s2 + lane_xor2(s2));
     // butterflies at strides 1..32 in the lane, 64 and 128 across the quarters
     fwht(x);
-#pragma unroll
-    for (int j = 0; j < 64; ++j) x[j] = lane_xor1(x[j]) + x[j] * sgn1;
-#pragma unroll
-    for (int j = 0; j < 64; ++j) x[j] = lane_xor2(x[j]) + x[j] * sgn2;
+    // strides 64 and 128: lane q then holds its values times sgn1 * sgn2
+    // (+, -, -, + for q = 0..3), which the reciprocal norm takes back exactly
+    cross_stage<1>(x, sgn1);
+    cross_stage<2>(x, sgn2);
     uint32_t words[2 * BITS];
-    encode<BITS, 64>(x, ni.r, lds, 256u, __uint_as_float(HLWQ_KV_BUCKET_BIAS), words);
+    encode<BITS, 64>(x, ni.r * (sgn1 * sgn2), lds, 256u, __uint_as_float(HLWQ_KV_BUCKET_BIAS), words);
     // the batch's codes are contiguous: lane l's 8 BITS bytes at 8 BITS l
     lds_handover();
     if constexpr (BITS == 3) {
@@ -1123,6 +1171,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     const SwzLane linear{};
     stage_out<2, false>(a.packed + vec0 * kVec, p.nvalid * kVec, stage, lane, linear);
     if (q == 0u && v < p.nvalid) a.norms[vec0 + v] = ni.n16;
+    m = __builtin_amdgcn_readfirstlane(m_next);
+    b = blockIdx.x + gridDim.x * m;
   }
 }
 
@@ -1573,10 +1623,10 @@ int make_single(const void* w, const void* packed, const void* norms, int64_t n_
 // heads per launch, at most kMaxDispatch workgroups' worth of batches each.
 int launch_kv(bool quant, int bits, KvArgs a, int64_t bh, hipStream_t stream) {
   a.nbt = static_cast<uint32_t>(ceil_div(a.tq, kKvTokens));
-  // quantize: a persistent grid; dequantize: one batch per wave, workgroups
-  // handed out by the hardware (measured 12-15% faster for the KV dequantizer
-  // on a 2 x 4-head cache of 32768 tokens, 2-5% slower for the quantizer,
-  // whose workgroups first fill 4 KB of search tables)
+  // quantize: one 16-wave workgroup per CU drawing from its work pool (5%
+  // faster than a fixed share per wave on a 2 x 4-head cache of 32768
+  // tokens); dequantize: one batch per wave, workgroups handed out by the
+  // hardware (12-15% faster than a persistent grid)
   a.chunk = quant ? 0u : static_cast<uint32_t>(kWaves);
   const int64_t max_batches = static_cast<int64_t>(kWaves) * kMaxDispatch;
   if (a.nbt > max_batches) return HLWQ_ERR_LIMIT;
@@ -1589,8 +1639,8 @@ int launch_kv(bool quant, int bits, KvArgs a, int64_t bh, hipStream_t stream) {
     l.packed += h0 * a.out_stride * vec_bytes;
     l.norms += h0 * a.out_stride;
     l.total_batches = static_cast<uint32_t>(nh * a.nbt);
-    const dim3 grid(quant ? persistent_grid(l.total_batches, 4) : (l.total_batches + l.chunk - 1) / l.chunk),
-        block(kThreads);
+    const dim3 grid(quant ? persistent_grid(l.total_batches, 1, kKvPoolWaves) : (l.total_batches + l.chunk - 1) / l.chunk),
+        block(quant ? kKvPoolThreads : kThreads);
     if (quant) {
       if (bits == 3) hipLaunchKernelGGL(hlwq_kv_quantize_kernel<3>, grid, block, 0, stream, l);
       else hipLaunchKernelGGL(hlwq_kv_quantize_kernel<2>, grid, block, 0, stream, l);
