@@ -7,21 +7,31 @@ layer, 256 experts, gate_up [256, 1024, 2048] and down [256, 2048, 512] bf16
 result (one grouped launch).  Inputs are seeded synthetic N(0, 0.02^2) values
 with 0.1 % of each expert's entries scaled by 20, resident in HBM before timing
 starts; the step's working set (5.8 GB) is far larger than the 256 MB
-Infinity Cache, so every step streams from HBM.
+Infinity Cache, so every step streams from HBM.  The same run then times the
+Gemma-4-26B-A4B-shaped bank (gate_up [128, 1408, 2816], down [128, 2816, 704])
+the same way and reports it under "gemma4_moe_bank".
 
 Other workloads (--config) use the same procedure: the Gemma-4-26B-A4B-shaped
-bank, the dense hidden-5120 Linears (Q5 or --bits 3; dense_5120_int4 follows
-the quantize with the fused dequantize -> INT4), the H256 KV cache (Q3 or
---bits 2; three independent caches rotate so the working set exceeds the
+bank alone, the dense hidden-5120 Linears (Q5 or --bits 3; dense_5120_int4
+follows the quantize with the fused dequantize -> INT4), the H256 KV cache (Q3
+or --bits 2; three independent caches rotate so the working set exceeds the
 cache), the whole prompt appended to an empty streaming cache in one call
 (kv_h256_prefill), the streaming KV decode step (kv_h256_decode,
 latency-bound), and TQ3 on the Qwen3.6-shaped bank (qwen36_moe_bank_tq3).
 --layout codes8 stores one code per byte.
 
+Before any warm-up step, the run measures the streaming ceiling of each
+kernel's own read:write mix (libhlwq_stream, include/hlwq_stream.h: the same
+1 KB-contiguous loads and stores with no arithmetic, best of a few wave and
+unit shapes), then runs the workload's own steps for 0.3 s ("settle" in the
+output: from idle the card needs ~20 ms of these kernels to reach its steady
+clocks), so the W warm-up steps and the K timed steps run at the clocks a
+long quantization job sees.
+
 Prints one JSON line: weights/s of quantize + dequantize, with the per-kernel
 HBM roofline (algorithmic bytes / kernel time from HIP events on the launch
-stream), a measured device-to-device copy ceiling, and the CPU oracle timed
-on a bounded sample of the same workload.
+stream), each kernel's fraction of its mix's streaming ceiling, and the CPU
+oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 1000] [--config NAME] [--bits 5|3|2] [--layout packed|codes8]
 """
@@ -115,33 +125,85 @@ def stored_traffic(config, bits):
 _CACHE_SAFE_BYTES = 1 << 30
 
 
-def copy_ceiling(torch, dev, nbytes, reps=10):
-    """Device-to-device copy moving the same number of bytes (half read, half
-    written) as one quantize or dequantize launch: a practical HBM ceiling.
-    Below 1 GiB the copy rotates over several buffer pairs, so it streams from
-    HBM and not from the memory-side cache."""
-    n = max(nbytes // 8, 1 << 20)
-    pairs = max(1, min(16, -(-_CACHE_SAFE_BYTES // (8 * n))))
-    bufs = []
-    for _ in range(pairs):
-        src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
-        bufs.append((src, torch.empty_like(src)))
-    for src, dst in bufs:
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for r in range(reps):
-        src, dst = bufs[r % pairs]
-        dst.copy_(src)
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / reps
-    moved = 2 * n * 4
-    del bufs
-    return {"gbs": round(moved / (ms * 1e-3) / 1e9, 1), "bytes": moved, "ms": round(ms, 4), "buffer_pairs": pairs,
-            "kernel": "torch copy_ (float32 device-to-device)"}
+# (variant, 4-wave workgroups per CU, bytes of the larger side of a unit):
+# the kernels' own shape first (load 16 KB, wait, store; two workgroups per
+# CU), then the shapes a sweep found fastest on MI355X (one or two workgroups
+# per CU, larger units or double-buffered smaller ones)
+CEILING_SHAPES = [(0, 2, 16384), (1, 1, 16384), (1, 1, 32768), (2, 1, 16384), (2, 1, 8192), (3, 1, 4096),
+                  (3, 2, 4096)]
+_STREAM_MAX_READ = {0: 16384, 1: 32768, 2: 16384, 3: 4096}
+
+
+class StreamCeiling:
+    """Streaming ceilings of a read:write mix on the current device."""
+
+    def __init__(self, torch, dev, read_max, write_max):
+        import ctypes
+        from weight_quantization_amd import build as wqb
+        if not os.path.exists(wqb.STREAM_LIB):
+            raise RuntimeError(f"{wqb.STREAM_LIB} is missing: build it with __graft_entry__.build()")
+        self.lib = ctypes.CDLL(wqb.STREAM_LIB)
+        f = self.lib.hlwq_stream_mix
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                      ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        self.torch = torch
+        # at least 1 GiB each, and consecutive launches start at rotating
+        # offsets, so a small mix streams from HBM and not from the 256 MB
+        # memory-side cache (as the kernels' rotating input sets do)
+        self.src = torch.empty(max(read_max, _CACHE_SAFE_BYTES) + 65536, dtype=torch.uint8, device=dev)
+        self.dst = torch.empty(max(write_max, _CACHE_SAFE_BYTES) + 65536, dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream()
+        self.k = 0
+
+    def _launch(self, r, w, units, variant, wpc):
+        import ctypes
+        rspan, wspan = self.src.numel() - units * r, self.dst.numel() - units * w
+        ro = (self.k * units * r) % rspan // 256 * 256 if rspan > 0 else 0
+        wo = (self.k * units * w) % wspan // 256 * 256 if wspan > 0 else 0
+        self.k += 1
+        st = self.lib.hlwq_stream_mix(self.src.data_ptr() + ro, self.dst.data_ptr() + wo, r, w, units, variant, wpc,
+                                      ctypes.c_void_p(self.stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"hlwq_stream_mix failed with status {st}")
+
+    def warm(self, seconds=1.0):
+        """Stream for about `seconds` (the kernels' own shape, quantize mix)."""
+        units = min(self.src.numel() // 16384, self.dst.numel() // 5248)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(50):
+                self._launch(16384, 5248, units, 0, 2)
+            self.torch.cuda.synchronize()
+
+    def measure(self, read_total, write_total, reps=10):
+        """Best GB/s over CEILING_SHAPES for a launch reading `read_total` and
+        writing `write_total` bytes (units scaled to the same mix)."""
+        torch = self.torch
+        big_is_read = read_total >= write_total
+        ratio = min(read_total, write_total) / max(read_total, write_total)
+        rows = []
+        for variant, wpc, big in CEILING_SHAPES:
+            small = max(16, int(round(big * ratio / 16.0)) * 16)
+            r, w = (big, small) if big_is_read else (small, big)
+            if r > _STREAM_MAX_READ[variant] or w > 32768:
+                continue
+            units = int(min(read_total // r, write_total // w, self.src.numel() // r, self.dst.numel() // w))
+            for _ in range(2):
+                self._launch(r, w, units, variant, wpc)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ms = []
+            for _ in range(reps):
+                e0.record(self.stream)
+                self._launch(r, w, units, variant, wpc)
+                e1.record(self.stream)
+                e1.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            t = float(np.median(ms))
+            rows.append({"variant": variant, "workgroups_per_cu": wpc, "unit_read": r, "unit_write": w,
+                         "ms": round(t, 4), "gbs": round(units * (r + w) / (t * 1e-3) / 1e9, 1)})
+        best = max(rows, key=lambda x: x["gbs"])
+        return {"gbs": best["gbs"], "best": best, "shapes": rows}
 
 
 def to_device(torch, dev, bits_u16):
@@ -159,6 +221,8 @@ def weight_workload(torch, wq, dev, config, bits, layout="packed"):
         shapes.append((shape if len(shape) == 3 else (1, *shape)))
     field = 8 if layout == "codes8" else bits   # bits per stored code
     nbytes = algorithmic_bytes(shapes, field, 4 if tq3 else 2)
+    w_bytes = sum(E * o * i * 2 for E, o, i in shapes)   # bf16 of the real columns
+    c_bytes = nbytes - w_bytes                           # codes + norms
     copies = 1 if nbytes >= _CACHE_SAFE_BYTES else 2
     sets = []
     for c in range(copies):
@@ -209,7 +273,9 @@ def weight_workload(torch, wq, dev, config, bits, layout="packed"):
         "dequantize": dequant,
         "weights": sum(E * o * i for E, o, i in shapes),
         "bytes": nbytes,
-        "kernels": ((f"hlwq_quantize_kernel<3, 3, true>", f"hlwq_dequantize_kernel<3, 3, true>") if tq3 else
+        "rw": (w_bytes, c_bytes),      # quantize: read, write
+        "rw_d": (c_bytes, w_bytes),    # dequantize: read, write
+        "kernels": ((f"hlwq_quantize_kernel<3, 3, 2>", f"hlwq_dequantize_kernel<3, 3, 2>") if tq3 else
                     (f"hlwq_quantize_kernel<{bits}, {field}>", f"hlwq_dequantize_kernel<{bits}, {field}>")),
         "launches": len(shapes) if layout == "codes8" else 1,
         "copies": copies,
@@ -254,6 +320,8 @@ def int4_workload(torch, wq, dev, bits, config="dense_5120", copies=2):
         "bytes": algorithmic_bytes([(1, o, i) for o, i in shapes], bits),
         # codes + norm in; 64 B of nibbles + fp32 scale + u8 zero point out, per 128 weights
         "bytes_d": blocks * (16 * bits + 2 + 64 + 4 + 1),
+        "rw": (weights * 2, blocks * (16 * bits + 2)),
+        "rw_d": (blocks * (16 * bits + 2), blocks * (64 + 4 + 1)),
         "kernels": (f"hlwq_quantize_kernel<{bits}>", f"hlwq_dequantize_int4_kernel<{bits}>"),
         "launches": 1,
         "launches_d": len(shapes),
@@ -293,6 +361,8 @@ def kv_workload(torch, wq, dev, copies=3, n_residual=128, bits=3):
         "dequantize": dequant,
         "weights": elems,
         "bytes": elems * 2 + 2 * B * H * tq * (32 * bits + 2),
+        "rw": (elems * 2, 2 * B * H * tq * (32 * bits + 2)),
+        "rw_d": (2 * B * H * tq * (32 * bits + 2), elems * 2),
         "kernels": ("hlwq_kv_quantize_kernel", "hlwq_kv_dequantize_kernel"),
         "launches": 1,
         "copies": copies,
@@ -336,6 +406,8 @@ def prefill_workload(torch, wq, dev, copies=3, n_residual=128, bits=3):
         "bytes": elems * 2 + vec_out + 2 * B * H * n_residual * D * 2,
         # codes and norms in, bf16 of the encoded tokens out
         "bytes_d": vec_out + 2 * B * H * cap * D * 2,
+        "rw": (elems * 2, vec_out + 2 * B * H * n_residual * D * 2),
+        "rw_d": (vec_out, 2 * B * H * cap * D * 2),
         "kernels": ("hlwq_kv_append (hlwq_kv_quantize_kernel, then hlwq_kv_ring_fill_kernel for the window)",
                     "hlwq_kv_dequantize_kernel"),
         "launches": 2,
@@ -422,7 +494,7 @@ def decode_main(args, bits):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": DESCRIPTIONS["kv_h256_decode"], "name": "kv_h256_decode", "bits": bits,
                    "vectors_per_step": vectors},
@@ -492,17 +564,33 @@ def _oracle_worker(args):
     return done, time.perf_counter() - t0
 
 
+def _pool_map(n, args):
+    """Run _oracle_worker over `args` on n forked processes; the pool is
+    closed and joined, so no worker outlives the call."""
+    import multiprocessing as mp
+    pool = mp.get_context("fork").Pool(n)
+    try:
+        return pool.map(_oracle_worker, args)
+    finally:
+        pool.close()
+        pool.join()
+
+
+# One GPU's share of a GPU box's host is 16 cores, whatever the affinity mask
+# shows; the pool uses every core of the mask up to that share.
+HOST_SHARE_CORES = 16
+
+
 def cpu_baseline(config, bits, budget_s=10.0):
     """The oracle (fp32 canonical tier, plain numpy, untouched) on the host
-    cores: one forked process per core (at most 16), each quantizing and
-    dequantizing its own slice of the workload for `budget_s` seconds.  Inputs
-    are drawn before each worker's clock starts; only oracle calls are timed."""
-    import multiprocessing as mp
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
-    with mp.get_context("fork").Pool(1) as pool:  # one process alone on the host
-        single = pool.map(_oracle_worker, [(config, bits, 0, budget_s / 2)])[0]
-    with mp.get_context("fork").Pool(cores) as pool:
-        res = pool.map(_oracle_worker, [(config, bits, k, budget_s) for k in range(cores)])
+    cores: one forked process per core (every core of the affinity mask, at
+    most one GPU's share of the host), each quantizing and dequantizing its own
+    slice of the workload for `budget_s` seconds.  Inputs are drawn before each
+    worker's clock starts; only oracle calls are timed."""
+    mask = len(os.sched_getaffinity(0))
+    cores = max(1, min(HOST_SHARE_CORES, mask))
+    single = _pool_map(1, [(config, bits, 0, budget_s / 2)])[0]  # one process alone on the host
+    res = _pool_map(cores, [(config, bits, k, budget_s) for k in range(cores)])
     done = sum(r[0] for r in res)
     wall = max(r[1] for r in res)
     what = ("1024 tokens of one KV head" if config in ("kv_h256", "kv_h256_prefill")
@@ -511,9 +599,11 @@ def cpu_baseline(config, bits, budget_s=10.0):
         "value": done / wall,
         "unit": "weights/s",
         "cores": cores,
+        "affinity_cores": mask,
         "kind": "oracle",
         "single_process": {"value": single[0] / single[1], "seconds": round(single[1], 2)},
-        "sample": f"{cores} processes x {budget_s:.0f} s, each on {what} of {config} "
+        "sample": f"{cores} processes x {budget_s:.0f} s (every core of the {mask}-core affinity mask, "
+                  f"at most {HOST_SHARE_CORES}: one GPU's share of the host), each on {what} of {config} "
                   f"({'TQ3' if config.endswith('_tq3') else f'Q{bits}'} quantize+"
                   f"{'dequantize to INT4' if config == 'dense_5120_int4' else 'dequantize'}, repeated): "
                   f"{done} weights in {wall:.1f} s; "
@@ -521,16 +611,118 @@ def cpu_baseline(config, bits, budget_s=10.0):
     }
 
 
+def make_workload(torch, wq, dev, config, bits, layout):
+    if config == "kv_h256":
+        return kv_workload(torch, wq, dev, bits=bits)
+    if config == "kv_h256_prefill":
+        return prefill_workload(torch, wq, dev, bits=bits)
+    if config == "dense_5120_int4":
+        return int4_workload(torch, wq, dev, bits)
+    return weight_workload(torch, wq, dev, config, bits, layout=layout)
+
+
+SETTLE_S = 0.3
+
+
+def settle(torch, wl, seconds=SETTLE_S):
+    """Run the workload's steps for `seconds` before the warm-up steps.  From
+    idle, the card takes about 25 steps (~20 ms) of these kernels to reach its
+    steady clocks, and pure streaming does not bring it there; a
+    quantization job of a whole model runs for seconds at the steady rate,
+    which is what the K timed steps measure.  Returns the steps run."""
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            wl["quantize"]()
+            wl["dequantize"]()
+        n += 20
+        torch.cuda.synchronize()
+    return n
+
+
+def time_workload(torch, wl, steps, warmup):
+    """W untimed steps, then K timed steps between two synchronisations; HIP
+    events on the launch stream around each kernel.  Returns per-step quantize
+    and dequantize ms and the wall time of the K steps."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        wl["quantize"]()
+        wl["dequantize"]()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        wl["quantize"]()
+        ev[s][1].record(stream)
+        wl["dequantize"]()
+        ev[s][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q_ms = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in range(steps)])
+    d_ms = np.array([ev[s][1].elapsed_time(ev[s][2]) for s in range(steps)])
+    return q_ms, d_ms, wall
+
+
+def leg(ms, nbytes, weights, ceiling):
+    """Timing summary of one kernel (leg of the step): GB/s are algorithmic
+    bytes over the mean time; fractions of the 8 TB/s peak and of the
+    streaming ceiling of the same read:write mix."""
+    gbs = nbytes / (ms.mean() * 1e-3) / 1e9
+    out = {"ms": round(float(ms.mean()), 4), "ms_median": round(float(np.median(ms)), 4),
+           "ms_min": round(float(ms.min()), 4), "ms_max": round(float(ms.max()), 4),
+           "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "weights_per_s": weights / (ms.mean() * 1e-3)}
+    if ceiling is not None:
+        out["ceiling_gbs"] = ceiling["gbs"]
+        out["frac_of_ceiling"] = round(gbs / ceiling["gbs"], 4)
+    return out
+
+
+def ceilings(ceil, wl):
+    q = ceil.measure(*wl["rw"])
+    d = ceil.measure(*wl["rw_d"])
+    return {"kernel": "hlwq_stream_mix (libhlwq_stream.so): the kernels' loads and stores without arithmetic",
+            "quantize_mix": {"read_bytes": wl["rw"][0], "write_bytes": wl["rw"][1], **q},
+            "dequantize_mix": {"read_bytes": wl["rw_d"][0], "write_bytes": wl["rw_d"][1], **d}}
+
+
+def extra_bank(torch, wq, dev, ceil, config, bits, steps, warmup):
+    """Time a second MoE-bank workload the same way (its own ceilings too)."""
+    print(f"[bench] generating {config}", file=sys.stderr, flush=True)
+    wl = make_workload(torch, wq, dev, config, bits, "packed")
+    torch.cuda.synchronize()
+    ceil.warm(1.0)
+    c = ceilings(ceil, wl)
+    n_settle = settle(torch, wl)
+    print(f"[bench] timing {steps} steps of {config}", file=sys.stderr, flush=True)
+    q_ms, d_ms, wall = time_workload(torch, wl, steps, warmup)
+    weights, nbytes = wl["weights"], wl["bytes"]
+    step_gbs = 2 * nbytes / (wall / steps) / 1e9
+    out = {"workload": DESCRIPTIONS[config], "weights": weights, "bits": bits, "steps": steps, "warmup": warmup,
+           "algorithmic_bytes_per_launch": nbytes, "ms_per_step": round(wall * 1e3 / steps, 4),
+           "weights_per_s": weights / (wall / steps), "hbm_gbs": round(step_gbs, 1),
+           "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+           "settle": {"seconds": SETTLE_S, "steps": n_settle},
+           "quantize": leg(q_ms, nbytes, weights, c["quantize_mix"]),
+           "dequantize": leg(d_ms, nbytes, weights, c["dequantize_mix"]),
+           "ceiling": c}
+    del wl
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # the card needs a few hundred milliseconds of sustained load to reach its
-    # steady clocks; 1000 untimed steps is about 0.8 s on the default workload
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--config", default="qwen36_moe_bank", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--bits", type=int, default=None, choices=(5, 3, 2))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-bank", action="store_true",
+                    help="skip the Gemma-4-shaped bank the default run also times")
     ap.add_argument("--layout", default="packed", choices=("packed", "codes8"),
                     help="weight codes packed (bits per code) or one code per byte")
     args = ap.parse_args()
@@ -564,43 +756,34 @@ def main():
     torch.cuda.set_device(dev)
 
     print(f"[bench] generating {config}", file=sys.stderr, flush=True)
-    if config == "kv_h256":
-        wl = kv_workload(torch, wq, dev, bits=bits)
-    elif config == "kv_h256_prefill":
-        wl = prefill_workload(torch, wq, dev, bits=bits)
-    elif config == "dense_5120_int4":
-        wl = int4_workload(torch, wq, dev, bits)
-    else:
-        wl = weight_workload(torch, wq, dev, config, bits, layout=args.layout)
+    wl = make_workload(torch, wq, dev, config, bits, args.layout)
     weights, bytes_dir, launches = wl["weights"], wl["bytes"], wl["launches"]
     bytes_d = wl.get("bytes_d", bytes_dir)  # the second leg may move other bytes (INT4 output)
     launches_d = wl.get("launches_d", launches)
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        wl["quantize"]()
-        wl["dequantize"]()
-    torch.cuda.synchronize()
+    # the headline bank's run also times the other MoE bank
+    extra = None
+    if config == "qwen36_moe_bank" and bits == 5 and args.layout == "packed" and not args.no_extra_bank:
+        extra = "gemma4_moe_bank"
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # streaming ceilings of both kernels' mixes; about a second of streaming
+    # first, which also brings the card to its steady clocks
+    rmax = max(wl["rw"][0], wl["rw_d"][0])
+    wmax = max(wl["rw"][1], wl["rw_d"][1])
+    if extra is not None:
+        gb = sum(E * o * i * 2 for E, o, i in (synth.CONFIGS[extra][t][1] for t in synth.CONFIGS[extra]))
+        rmax, wmax = max(rmax, gb), max(wmax, gb)
+    print("[bench] measuring the streaming ceilings", file=sys.stderr, flush=True)
+    ceil = StreamCeiling(torch, dev, rmax, wmax)
+    ceil.warm(1.0)
+    ceiling = ceilings(ceil, wl)
+    n_settle = settle(torch, wl)
+
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        ev[s][0].record(stream)
-        wl["quantize"]()
-        ev[s][1].record(stream)
-        wl["dequantize"]()
-        ev[s][2].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    q_ms = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in range(args.steps)])
-    d_ms = np.array([ev[s][1].elapsed_time(ev[s][2]) for s in range(args.steps)])
+    q_ms, d_ms, wall = time_workload(torch, wl, args.steps, args.warmup)
     ms_per_step = wall * 1e3 / args.steps
 
-    q_gbs = bytes_dir / (q_ms.mean() * 1e-3) / 1e9
-    d_gbs = bytes_d / (d_ms.mean() * 1e-3) / 1e9
     dom = 0 if q_ms.mean() >= d_ms.mean() else 1
     dom_ms = max(q_ms.mean(), d_ms.mean())
     dom_bytes, dom_launches = (bytes_dir, launches) if dom == 0 else (bytes_d, launches_d)
@@ -630,24 +813,29 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
+        # the arithmetic is fp32 (norms, butterflies, compares); weights are
+        # read and written as bf16
         "dtype": "f32",
+        "io_dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": DESCRIPTIONS[config], "name": config, "weights": weights, "bits": bits,
                    "block": 256 if config.startswith("kv_") else 128, "input_sets": wl["copies"],
                    "layout": "packed" if config.startswith("kv_") else args.layout},
         "hbm_gbs": round(step_gbs, 1),
         "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
-        "quantize": {"ms": round(float(q_ms.mean()), 4), "ms_median": round(float(np.median(q_ms)), 4),
-                     "ms_min": round(float(q_ms.min()), 4), "ms_max": round(float(q_ms.max()), 4),
-                     "gbs": round(q_gbs, 1), "weights_per_s": weights / (q_ms.mean() * 1e-3)},
-        "dequantize": {"ms": round(float(d_ms.mean()), 4), "ms_median": round(float(np.median(d_ms)), 4),
-                       "ms_min": round(float(d_ms.min()), 4), "ms_max": round(float(d_ms.max()), 4),
-                       "gbs": round(d_gbs, 1), "weights_per_s": weights / (d_ms.mean() * 1e-3)},
+        # untimed steps run before the W warm-up steps, until the card's
+        # clocks have settled (see settle())
+        "settle": {"seconds": SETTLE_S, "steps": n_settle},
+        "quantize": leg(q_ms, bytes_dir, weights, ceiling["quantize_mix"]),
+        "dequantize": leg(d_ms, bytes_d, weights, ceiling["dequantize_mix"]),
         "roofline": roofline,
+        "ceiling": ceiling,
     }
-    result["copy_ceiling"] = copy_ceiling(torch, dev, bytes_dir // launches)
-    result["copy_frac"] = round(step_gbs / result["copy_ceiling"]["gbs"], 4)
     del wl
+    torch.cuda.empty_cache()
+    if extra is not None:
+        result[extra] = extra_bank(torch, wq, dev, ceil, extra, bits, args.steps, args.warmup)
+    del ceil
     torch.cuda.empty_cache()
     if cpu is not None:
         result["cpu_baseline"] = cpu

@@ -279,3 +279,28 @@ def test_binding_rejects_host_tensors():
         wq.hlwq_tq3_quantize(w)
     with pytest.raises(TypeError):
         wq.hlwq_quantize(w.float(), 5)
+
+
+def test_stream_probe_library_exports_and_validates():
+    # libhlwq_stream (include/hlwq_stream.h) is bench.py's ceiling probe; it
+    # loads without a GPU and rejects bad arguments before any HIP call
+    import re
+    from weight_quantization_amd import build as wqb
+    text = re.sub(r"/\*.*?\*/", "", open(wqb.INCLUDE + "/hlwq_stream.h").read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(hlwq_[a-z_0-9]+)\s*\(", text)))
+    assert names == ["hlwq_stream_mix"]
+    s = ctypes.CDLL(wqb.STREAM_LIB)
+    f = s.hlwq_stream_mix
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    buf = ctypes.c_void_p(4096)  # never dereferenced: every call below fails validation or has no work
+    assert f(buf, buf, 16384, 5248, 10, 4, 1, None) == -3          # unknown variant
+    assert f(buf, buf, 16384, 5248, 10, 0, 0, None) == -3          # workgroups per CU outside 1..4
+    assert f(buf, buf, 16384, 5248, 10, 3, 1, None) == -2          # read unit too large for variant 3
+    assert f(buf, buf, 100, 5248, 10, 0, 1, None) == -2            # not a multiple of 16
+    assert f(buf, buf, 16384, 0, 10, 0, 1, None) == -2             # nothing written
+    assert f(buf, buf, 16384, 65536, 10, 0, 1, None) == -2         # write unit above 32 KB
+    assert f(None, buf, 16384, 5248, 10, 0, 1, None) == -1         # NULL
+    assert f(ctypes.c_void_p(4100), buf, 16384, 5248, 10, 0, 1, None) == -6  # misaligned
+    assert f(None, None, 16384, 5248, 0, 0, 1, None) == 0          # zero units: nothing to do

@@ -4,7 +4,9 @@ Steps:
 1. compile and run the host table generator (Lloyd-Max codebooks and the
    bucket-search tables, verified by brute force while generating);
 2. compile the kernels and the C ABI with hipcc into ``libhlwq.so`` next to
-   this file.
+   this file;
+3. compile the streaming-bandwidth probe that bench.py uses as its HBM ceiling
+   into ``libhlwq_stream.so`` (include/hlwq_stream.h).
 
 Run ``python -m weight_quantization_amd.build`` or call ``build()``.
 """
@@ -21,6 +23,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libhlwq.so")
+STREAM_LIB = os.path.join(HERE, "libhlwq_stream.so")
 
 ARCH = "gfx950"
 
@@ -34,6 +37,9 @@ HIPCC_FLAGS = [
     "-ffp-contract=off",
     # correctly rounded fp32 division and sqrt (the norm and its reciprocal)
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # fp32 denormals kept, not flushed: the code search forms its bucket index
+    # as a denormal, and blocks of tiny values have denormal squares
+    "-fno-gpu-flush-denormals-to-zero",
     # keep fp32 arithmetic on unpacked VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
@@ -75,10 +81,18 @@ def build_library(extra_flags=(), out: str = LIB, source: str | None = None) -> 
     return out
 
 
+def build_stream_library(out: str = STREAM_LIB) -> str:
+    tmp = out + ".tmp"
+    _run([_hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, os.path.join(CSRC, "stream_ceiling.hip"), "-o", tmp])
+    os.replace(tmp, out)
+    return out
+
+
 def build(verbose: bool = True) -> str:
     path = build_library()
+    stream = build_stream_library()
     if verbose:
-        print(f"built {path}", file=sys.stderr)
+        print(f"built {path} and {stream}", file=sys.stderr)
     return path
 
 
