@@ -135,8 +135,10 @@ int hlwq_dequantize_codes8(const void* codes_u8, const void* norms_f16, int64_t 
  *   inverse : bf16 of D1 H D2 c[codes] * (norm / 128).
  * Fixed fp32 operation order, shared with the HLWQ kernels where the steps
  * coincide: the norm tree, 1 / n and the butterflies as above, y's sign flip
- * after the rounding of z * (1 / n); rho^2 is the adjacent-pair tree over
- * RN(c^2) (level 0 RN(e0 + e1)), rho and n / t correctly rounded,
+ * after the rounding of z * (1 / n); rho^2 is the exact sum of the 128
+ * RN(c^2) of the selected centroids, rounded once to fp32 (each RN(c^2) is a
+ * multiple of 2^-28 and the sum is below 2^10, so the sum itself is exact),
+ * rho and n / t correctly rounded,
  * t = RN(rho * RN(1 / sqrt(128))); the inverse multiplies by RN(norm * 2^-7)
  * and flips D1's signs after rounding.  Layouts: packed u8
  * [n_mats][out][ng][48] in the 3-bit packing above (ng = ceil(in / 128)),

@@ -3,6 +3,7 @@
  * of the device entry points (no kernel is launched).  Exit status 0 on
  * success; prints the first failed check otherwise. */
 #include <stdio.h>
+#include <stdint.h>
 #include <string.h>
 
 #include "hlwq.h"
@@ -48,6 +49,60 @@ int main(void) {
   CHECK(hlwq_quantize_grouped(&d, 1, 5, NULL) == HLWQ_ERR_NULL);
   CHECK(hlwq_tq3_quantize_grouped(&d, 1, 42, NULL) == HLWQ_ERR_NULL);
   CHECK(strlen(hlwq_status_string(HLWQ_ERR_ALIGN)) > 0);
+  CHECK(strcmp(hlwq_status_string(-99), "unknown status") == 0);
+
+  /* sizes whose byte counts overflow int64 are refused, not wrapped */
+  CHECK(hlwq_packed_bytes(INT64_MAX, 1 << 20, 128, 5) == 0u);
+  CHECK(hlwq_packed_bytes(4, 256, 100, 5) == 0u && hlwq_packed_bytes(4, 256, 128, 9) == 0u);
+  CHECK(hlwq_norm_count(-1, 128, 128) == 0u && hlwq_norm_count(INT64_MAX, 1 << 30, 128) == 0u);
+  CHECK(hlwq_quantize(buf, INT64_MAX, 2, 128, 128, 5, buf, buf, NULL) == HLWQ_ERR_SHAPE);
+  CHECK(hlwq_quantize(buf, 1, -1, 128, 128, 5, buf, buf, NULL) == HLWQ_ERR_SHAPE);
+  d.w = buf;
+  d.packed = buf;
+  d.norms = buf;
+  d.rows = (int64_t)1 << 40;
+  d.in = (int64_t)1 << 40;
+  CHECK(hlwq_quantize_grouped(&d, 1, 5, NULL) == HLWQ_ERR_SHAPE);
+  d.rows = (int64_t)1 << 32; /* 2^32 blocks: more than one matrix may hold */
+  d.in = 128;
+  CHECK(hlwq_quantize_grouped(&d, 1, 5, NULL) == HLWQ_ERR_LIMIT);
+  CHECK(hlwq_dequantize_grouped(&d, 1, 3, NULL) == HLWQ_ERR_LIMIT);
+  CHECK(hlwq_quantize_grouped(&d, -1, 5, NULL) == HLWQ_ERR_SHAPE);
+  CHECK(hlwq_quantize_grouped(NULL, 1, 5, NULL) == HLWQ_ERR_NULL);
+  CHECK(hlwq_quantize_grouped(&d, 1, 4, NULL) == HLWQ_ERR_BITS);
+  /* misaligned code buffer */
+  d.rows = 4;
+  d.packed = buf + 1;
+  CHECK(hlwq_quantize_grouped(&d, 1, 5, NULL) == HLWQ_ERR_ALIGN);
+  CHECK(hlwq_quantize_codes8(buf, 1, 4, 128, 128, 5, buf + 1, buf, NULL) == HLWQ_ERR_ALIGN);
+  CHECK(hlwq_dequantize_codes8(buf, buf, 1, 4, 128, 128, 2, buf, NULL) == HLWQ_ERR_BITS);
+  /* TQ3: group 128 only, fp32 norms 4-byte aligned */
+  CHECK(hlwq_tq3_quantize(buf, 1, 4, 128, 64, 42, buf, buf, NULL) == HLWQ_ERR_BLOCK);
+  CHECK(hlwq_tq3_dequantize(buf, buf + 2, 1, 4, 128, 128, 42, buf, NULL) == HLWQ_ERR_ALIGN);
+  /* dequantize to INT4: whole 128-column groups only */
+  CHECK(hlwq_dequantize_int4(buf, buf, 1, 4, 200, 128, 5, buf, buf, buf, NULL) == HLWQ_ERR_SHAPE);
+  CHECK(hlwq_dequantize_int4(NULL, buf, 1, 4, 256, 128, 5, buf, buf, buf, NULL) == HLWQ_ERR_NULL);
+  CHECK(hlwq_dequantize_int4(buf, buf, 1, 4, 256, 128, 6, buf, buf, buf, NULL) == HLWQ_ERR_BITS);
+  /* KV cache */
+  CHECK(hlwq_kv_quantize(buf, 1, 4, 300, 256, 5, 128, buf, buf, NULL) == HLWQ_ERR_BITS);
+  CHECK(hlwq_kv_quantize(buf, 1, 4, -3, 256, 3, 128, buf, buf, NULL) == HLWQ_ERR_SHAPE);
+  CHECK(hlwq_kv_quantize(buf, 1, 4, 300, 256, 3, 128, buf + 8, buf, NULL) == HLWQ_ERR_ALIGN);
+  CHECK(hlwq_kv_quantize(buf, 1, 4, 100, 256, 3, 128, NULL, NULL, NULL) == HLWQ_OK); /* all tokens stay bf16 */
+  CHECK(hlwq_kv_dequantize(buf, buf, INT64_MAX, 4, 300, 256, 3, 128, buf, NULL) == HLWQ_ERR_SHAPE);
+  CHECK(hlwq_kv_append(buf, 1, 4, 1, 200, buf, 128, buf, buf, 300, 128, 3, NULL) == HLWQ_ERR_BLOCK);
+  CHECK(hlwq_kv_append(buf, 1, 4, 0, 200, buf, 128, buf, buf, 300, 256, 3, NULL) == HLWQ_OK); /* nothing new */
+  CHECK(hlwq_kv_append(buf, 1, 4, 1, 200, buf, 128, buf, buf, 50, 256, 3, NULL) == HLWQ_ERR_SHAPE); /* capacity */
+  CHECK(hlwq_kv_append(NULL, 1, 4, 1, 200, buf, 128, buf, buf, 300, 256, 3, NULL) == HLWQ_ERR_NULL);
+  /* search tables: a partial copy of the bucket bytes, every entry, the constants */
+  {
+    uint8_t bytes[16];
+    uint32_t entries[64];
+    float scale = 0.0f;
+    uint32_t bias = 0;
+    CHECK(hlwq_search_table(0, bytes, (int)sizeof(bytes), entries, &scale, &bias) > 16);
+    CHECK(scale > 0.0f && bias > 0u && entries[1] == 0u && entries[63] == 31u);
+    CHECK(hlwq_search_table(7, bytes, (int)sizeof(bytes), entries, &scale, &bias) == HLWQ_ERR_BITS);
+  }
   printf("c abi ok\n");
   return 0;
 }

@@ -64,6 +64,14 @@ namespace {
 
 const double kInf = std::numeric_limits<double>::infinity();
 
+// Extent of the brute-force checks: ulps probed on each side of every
+// threshold and bucket edge, and sweep points on each side of zero.  The build
+// uses the full check; HLWQ_GEN_QUICK=1 (the sanitizer test, which runs this
+// program under AddressSanitizer and UBSan) a smaller one.  The tables printed
+// do not depend on it.
+int g_near = 4096;
+int64_t g_sweep = 20000000;
+
 double gauss_pdf(double t) {
   if (std::isinf(t)) return 0.0;
   return std::exp(-0.5 * t * t) / std::sqrt(2.0 * M_PI);
@@ -192,7 +200,7 @@ Tables make_tables(int K, int buckets) {
   probes.push_back(0.0f);
   for (float p : probes) {
     float lo = p, hi = p;
-    for (int i = 0; i < 4096; ++i) {
+    for (int i = 0; i < g_near; ++i) {
       lo = std::nextafterf(lo, -INFINITY);
       hi = std::nextafterf(hi, INFINITY);
       for (float y : {lo, hi, p}) {
@@ -204,8 +212,8 @@ Tables make_tables(int K, int buckets) {
       }
     }
   }
-  for (int64_t i = -20000000; i <= 20000000; ++i) {
-    const float y = (float)((double)i * (ymax / 20000000.0));
+  for (int64_t i = -g_sweep; i <= g_sweep; ++i) {
+    const float y = (float)((double)i * (ymax / (double)g_sweep));
     if (count_code(tb.thr, y) != bucket_code(tb, y)) {
       std::fprintf(stderr, "gen_tables: bucket search wrong at y=%a\n", y);
       std::exit(1);
@@ -267,7 +275,7 @@ Tables mirror_tables(const Tables& tb) {
   probes.push_back(0.0f);
   for (float p : probes) {
     float lo = p, hi = p;
-    for (int i = 0; i < 4096; ++i) {
+    for (int i = 0; i < g_near; ++i) {
       lo = std::nextafterf(lo, -INFINITY);
       hi = std::nextafterf(hi, INFINITY);
       check(lo);
@@ -275,7 +283,7 @@ Tables mirror_tables(const Tables& tb) {
       check(p);
     }
   }
-  for (int64_t i = -20000000; i <= 20000000; ++i) check((float)((double)i * (ymax / 20000000.0)));
+  for (int64_t i = -g_sweep; i <= g_sweep; ++i) check((float)((double)i * (ymax / (double)g_sweep)));
   for (float y : {0.0f, -0.0f, 0x1p-149f, -0x1p-149f, 0x1p-126f, -0x1p-126f}) check(y);
   return m;
 }
@@ -308,6 +316,11 @@ void emit_bytes(const char* name, const std::vector<uint8_t>& v) {
 }  // namespace
 
 int main() {
+  const char* quick = std::getenv("HLWQ_GEN_QUICK");
+  if (quick && quick[0] == '1') {
+    g_near = 64;
+    g_sweep = 200000;
+  }
   const Tables q5 = make_tables(32, 2048);
   const Tables q3 = make_tables(8, 2048);
   const Tables kv3 = make_tables(8, 4096);
