@@ -284,9 +284,9 @@ def weight_workload(torch, wq, dev, config, bits, layout="packed"):
 
 
 def int4_workload(torch, wq, dev, bits, config="dense_5120", copies=2):
-    """HLWQ quantize of the dense Linears (one grouped launch), then one
-    dequantize-to-INT4 launch per matrix; two rotating sets, as for the other
-    small working sets."""
+    """HLWQ quantize of the dense Linears (one grouped launch), then the
+    dequantize to INT4 of all of them (one grouped launch); two rotating sets,
+    as for the other small working sets."""
     tensors = list(synth.CONFIGS[config])
     shapes = [tuple(synth.CONFIGS[config][t][1]) for t in tensors]
     sets = []
@@ -307,8 +307,7 @@ def int4_workload(torch, wq, dev, bits, config="dense_5120", copies=2):
 
     def to_int4():
         items, outs = sets[(state["i"] + 1) % copies]
-        for (w, p, n), (q4, sc, z) in zip(items, outs):
-            wq.hlwq_dequantize_int4(p, n, w.shape[-1], bits, q4=q4, scales=sc, zeros=z)
+        wq.hlwq_dequantize_int4_grouped([(p, n, q4, sc, z) for (w, p, n), (q4, sc, z) in zip(items, outs)], bits)
         state["i"] += 1
 
     weights = sum(o * i for o, i in shapes)
@@ -324,7 +323,7 @@ def int4_workload(torch, wq, dev, bits, config="dense_5120", copies=2):
         "rw_d": (blocks * (16 * bits + 2), blocks * (64 + 4 + 1)),
         "kernels": (f"hlwq_quantize_kernel<{bits}>", f"hlwq_dequantize_int4_kernel<{bits}>"),
         "launches": 1,
-        "launches_d": len(shapes),
+        "launches_d": 1,
         "copies": copies,
         "keep": sets,
     }

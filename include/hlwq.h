@@ -196,6 +196,26 @@ int hlwq_dequantize_grouped(const hlwq_mat_desc* mats, int n, int bits, void* hi
 int hlwq_dequantize_int4(const void* packed_u8, const void* norms_f16, int64_t n_mats, int64_t out, int64_t in,
                          int block, int bits, void* q4_u8, void* scales_f32, void* zeros_u8, void* hip_stream);
 
+/* One matrix of hlwq_dequantize_int4_grouped: `packed` / `norms` are read,
+ * `q4` / `scales` / `zeros` written, with the layouts and alignment of
+ * hlwq_dequantize_int4; `rows` = n_mats * out, `in` a multiple of 128. */
+typedef struct hlwq_int4_desc {
+  const void* packed;  /* u8   [rows][in / 128][16 * bits] */
+  const void* norms;   /* fp16 [rows][in / 128] */
+  void* q4;            /* u8   [rows][in / 2] */
+  void* scales;        /* fp32 [rows][in / 128] */
+  void* zeros;         /* u8   [rows][in / 128] */
+  int64_t rows;
+  int64_t in;
+} hlwq_int4_desc;
+
+/* hlwq_dequantize_int4 over several matrices (the Linears of a layer, say) in
+ * one launch, as hlwq_dequantize_grouped does for bf16: `mats` is a host array
+ * of n descriptors, read before the call returns; more than 16 descriptors are
+ * split over several launches.  bits 5 or 3; every descriptor is validated
+ * before anything is enqueued. */
+int hlwq_dequantize_int4_grouped(const hlwq_int4_desc* mats, int n, int bits, void* hip_stream);
+
 /* Quantize a KV cache [batch][heads][tokens][head_dim] (bf16) per head
  * vector: H256 rotation, 8 Lloyd-Max centroids, 3-bit codes ("Qwopus3.6-27B-v2
  * · HLWQ Q5", "Methodology notes", KV bullet), or with bits = 2 the 4-centroid

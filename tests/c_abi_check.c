@@ -83,6 +83,30 @@ int main(void) {
   CHECK(hlwq_dequantize_int4(buf, buf, 1, 4, 200, 128, 5, buf, buf, buf, NULL) == HLWQ_ERR_SHAPE);
   CHECK(hlwq_dequantize_int4(NULL, buf, 1, 4, 256, 128, 5, buf, buf, buf, NULL) == HLWQ_ERR_NULL);
   CHECK(hlwq_dequantize_int4(buf, buf, 1, 4, 256, 128, 6, buf, buf, buf, NULL) == HLWQ_ERR_BITS);
+  {
+    hlwq_int4_desc q;
+    q.packed = buf;
+    q.norms = buf;
+    q.q4 = buf;
+    q.scales = buf;
+    q.zeros = buf;
+    q.rows = 4;
+    q.in = 200;
+    CHECK(hlwq_dequantize_int4_grouped(&q, 1, 5, NULL) == HLWQ_ERR_SHAPE);  /* in not a multiple of 128 */
+    q.in = 256;
+    q.q4 = NULL;
+    CHECK(hlwq_dequantize_int4_grouped(&q, 1, 5, NULL) == HLWQ_ERR_NULL);
+    q.q4 = buf;
+    q.scales = buf + 2;
+    CHECK(hlwq_dequantize_int4_grouped(&q, 1, 5, NULL) == HLWQ_ERR_ALIGN);
+    q.rows = (int64_t)1 << 40;
+    q.in = (int64_t)1 << 40;
+    CHECK(hlwq_dequantize_int4_grouped(&q, 1, 3, NULL) == HLWQ_ERR_SHAPE);
+    CHECK(hlwq_dequantize_int4_grouped(&q, 1, 4, NULL) == HLWQ_ERR_BITS);
+    CHECK(hlwq_dequantize_int4_grouped(NULL, 1, 5, NULL) == HLWQ_ERR_NULL);
+    q.rows = 0;
+    CHECK(hlwq_dequantize_int4_grouped(&q, 1, 5, NULL) == HLWQ_OK);        /* nothing to do */
+  }
   /* KV cache */
   CHECK(hlwq_kv_quantize(buf, 1, 4, 300, 256, 5, 128, buf, buf, NULL) == HLWQ_ERR_BITS);
   CHECK(hlwq_kv_quantize(buf, 1, 4, -3, 256, 3, 128, buf, buf, NULL) == HLWQ_ERR_SHAPE);

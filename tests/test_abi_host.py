@@ -24,7 +24,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = wq.declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     raw = ctypes.CDLL(wq.binding.LIB_PATH)
     for name in names:
         assert hasattr(raw, name), name

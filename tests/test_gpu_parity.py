@@ -420,6 +420,40 @@ def test_codes8(wq, bits, shape):
     assert np.array_equal(bf16_bits(out2).reshape(want.shape), want)
 
 
+@pytest.mark.parametrize("bits", [5, 3])
+def test_dequantize_int4_grouped(wq, bits):
+    # 20 matrices of mixed shapes (a few empty) in one call: split over two
+    # launches of at most 16, each matrix equal to the oracle and to the
+    # single-matrix entry point
+    rng = np.random.default_rng(40 + bits)
+    host, items = [], []
+    for i in range(20):
+        rows = 0 if i in (3, 11) else int(rng.integers(1, 300))
+        n_in = 128 * int(rng.integers(1, 9))
+        wb = synth.random_bf16((rows, n_in), seed=500 + i, outlier_frac=0.001, outlier_mult=20.0)
+        nb = n_in // 128
+        packed, norms = wq.hlwq_quantize(to_dev(wb), bits)
+        items.append((packed, norms, torch.empty((rows, n_in // 2), dtype=torch.uint8, device="cuda"),
+                      torch.empty((rows, nb), dtype=torch.float32, device="cuda"),
+                      torch.empty((rows, nb), dtype=torch.uint8, device="cuda")))
+        host.append(wb)
+    _say("int4 grouped, 20 matrices, bits", bits)
+    wq.hlwq_dequantize_int4_grouped(items, bits)
+    torch.cuda.synchronize()
+    for (p, n, q4, sc, z), wb in zip(items, host):
+        if wb.shape[0] == 0:
+            continue
+        op, on = ref.quantize_c(wb, bits)
+        assert np.array_equal(p.cpu().numpy(), op)
+        p4, s4, z4 = ref.dequantize_to_int4_c(op, on, wb.shape[1], bits)
+        assert np.array_equal(q4.cpu().numpy(), p4)
+        assert np.array_equal(sc.cpu().numpy().view(np.uint32), s4.view(np.uint32))
+        assert np.array_equal(z.cpu().numpy(), z4)
+        q1, s1, z1 = wq.hlwq_dequantize_int4(p, n, wb.shape[1], bits)
+        torch.cuda.synchronize()
+        assert torch.equal(q1, q4) and torch.equal(s1, sc) and torch.equal(z1, z)
+
+
 def test_dequantize_int4_special_blocks(wq):
     w = _special_rows()
     w[8, ::2] = 0x8000

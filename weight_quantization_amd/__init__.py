@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     hlwq_dequantize_codes8,
     hlwq_dequantize_grouped,
     hlwq_dequantize_int4,
+    hlwq_dequantize_int4_grouped,
     hlwq_kv_append,
     hlwq_kv_dequantize,
     hlwq_kv_quantize,

@@ -29,6 +29,18 @@ class HLWQError(RuntimeError):
         self.status = status
 
 
+class Int4Desc(ctypes.Structure):
+    _fields_ = [
+        ("packed", ctypes.c_void_p),
+        ("norms", ctypes.c_void_p),
+        ("q4", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("zeros", ctypes.c_void_p),
+        ("rows", ctypes.c_int64),
+        ("in_", ctypes.c_int64),
+    ]
+
+
 class MatDesc(ctypes.Structure):
     _fields_ = [
         ("w", ctypes.c_void_p),
@@ -54,6 +66,7 @@ _SIGNATURES = {
     "hlwq_kv_dequantize": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _i64, _vp, _vp]),
     "hlwq_kv_append": (_int, [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _int, _int, _vp]),
     "hlwq_dequantize_int4": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp]),
+    "hlwq_dequantize_int4_grouped": (_int, [ctypes.POINTER(Int4Desc), _int, _int, _vp]),
     "hlwq_quantize_codes8": (_int, [_vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp]),
     "hlwq_dequantize_codes8": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp]),
     "hlwq_tq3_signs": (_int, [ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint32)]),
@@ -362,6 +375,31 @@ def hlwq_dequantize_int4(packed, norms, n_in: int, bits: int = 5, q4=None, scale
                                              _stream_handle(stream, packed, norms, q4, scales, zeros))
     _check("hlwq_dequantize_int4", st)
     return q4, scales, zeros
+
+
+def hlwq_dequantize_int4_grouped(items, bits: int = 5, stream=None):
+    """items: list of (packed u8 [.., out, nb, 16*bits], norms fp16 [.., out, nb],
+    q4 u8 [.., out, in / 2], scales fp32 [.., out, nb], zeros u8 [.., out, nb])
+    tuples, all preallocated; in = 128 nb.  One launch for up to 16 matrices."""
+    torch = _torch()
+    arr = (Int4Desc * max(len(items), 1))()
+    for i, (p, n, q4, sc, z) in enumerate(items):
+        _need(p, torch.uint8, "packed")
+        _need(n, torch.float16, "norms")
+        _need(q4, torch.uint8, "q4")
+        _need(sc, torch.float32, "scales")
+        _need(z, torch.uint8, "zeros")
+        if p.dim() < 2 or p.shape[-1] != 16 * bits:
+            raise ValueError("packed must be [.., out, nb, 16*bits]")
+        lead, nb = tuple(p.shape[:-2]), p.shape[-2]
+        if tuple(n.shape) != lead + (nb,) or tuple(sc.shape) != lead + (nb,) or tuple(z.shape) != lead + (nb,) or \
+                tuple(q4.shape) != lead + (nb * BLOCK // 2,):
+            raise ValueError("packed / norms / q4 / scales / zeros shape mismatch")
+        rows = int(np.prod(lead)) if lead else 1
+        arr[i] = Int4Desc(_ptr(p), _ptr(n), _ptr(q4), _ptr(sc), _ptr(z), rows, nb * BLOCK)
+    st = load_library().hlwq_dequantize_int4_grouped(arr, len(items), bits,
+                                                     _stream_handle(stream, *[t for item in items for t in item]))
+    _check("hlwq_dequantize_int4_grouped", st)
 
 
 def _descs(items):

@@ -381,10 +381,10 @@ __device__ __forceinline__ float recon_sumsq3(const uint32_t (&w)[12]) {
 }
 
 // Fill the pair table of a K-centroid codebook (K * K entries of 8 bytes).
-template <int BITS>
+template <int BITS, int NT = kThreads>
 __device__ __forceinline__ void fill_pairs(float* pairs, const float* __restrict__ cent) {
   constexpr int K = 1 << BITS;
-  for (int i = threadIdx.x; i < K * K; i += kThreads) {
+  for (int i = threadIdx.x; i < K * K; i += NT) {
     const float a = cent[i & (K - 1)], b = cent[i >> BITS];
     pairs[2 * i] = a + b;
     pairs[2 * i + 1] = a - b;
@@ -912,20 +912,30 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 // q = clamp(rint(w * inv) + zp, 0, 15), two codes per byte, low nibble first.
 // ---------------------------------------------------------------------------
 
-struct Int4Args {
-  const uint8_t* packed;   // [nblocks][16 * bits]
-  const uint16_t* norms;   // [nblocks]
-  uint8_t* q4;             // [nblocks][64]
-  float* scales;           // [nblocks]
-  uint8_t* zeros;          // [nblocks]
-  uint32_t nblocks, total_batches;
+// Up to kMaxGroup matrices per launch, batches of 64 blocks numbered over the
+// matrices in order (a prefix sum), as in the grouped weight kernels.
+struct Int4Group {
+  int32_t n;
+  uint32_t total_batches;
+  uint32_t batch_start[kMaxGroup + 1];
+  uint32_t nblocks[kMaxGroup];
+  const uint8_t* packed[kMaxGroup];   // [nblocks][16 * bits]
+  const uint16_t* norms[kMaxGroup];   // [nblocks]
+  uint8_t* q4[kMaxGroup];             // [nblocks][64]
+  float* scales[kMaxGroup];           // [nblocks]
+  uint8_t* zeros[kMaxGroup];          // [nblocks]
 };
 
-constexpr float kRoundMagic = 12582912.0f;       // 1.5 * 2^23: x + it rounds x to an integer, ties to even
-constexpr int32_t kRoundMagicBits = 0x4B400000;  // its bit pattern
+__device__ __forceinline__ int int4_group_of(const Int4Group& g, uint32_t b) {
+  int d = 0;
+  for (int i = 1; i < g.n; ++i) d = (b >= g.batch_start[i]) ? i : d;
+  return d;
+}
+
+constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23: x + it rounds x to an integer, ties to even
 
 template <int BITS>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_dequantize_int4_kernel(const Int4Args a) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) hlwq_dequantize_int4_kernel(const Int4Group a) {
   constexpr int kPairs = 8 << (2 * BITS);
   constexpr uint32_t kIn = 16 * BITS;  // packed bytes per block
   constexpr int kArea = 8192;          // per wave: the batch's codes in, then its nibbles out
@@ -942,13 +952,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 
   for (uint32_t b = blockIdx.x * kWaves + wave; b < a.total_batches; b += gridDim.x * kWaves) {
     refresh(sl, lane_a);
-    const uint32_t g0 = b * 64u;
-    const uint32_t left = a.nblocks - g0;
+    const int d = int4_group_of(a, b);
+    const uint32_t g0 = (b - a.batch_start[d]) * 64u;
+    const uint32_t left = a.nblocks[d] - g0;
     const uint32_t nvalid = left < 64u ? left : 64u;
     // lanes past the end of the batch repeat the last block and store nothing
     const uint32_t slot = static_cast<uint32_t>(lane) < nvalid ? static_cast<uint32_t>(lane) : nvalid - 1;
-    stage_in<BITS, false, 0>(a.packed + static_cast<size_t>(g0) * kIn, nvalid * kIn, area, lane, sl);
-    const float nscale = f16_value(a.norms[g0 + slot]) * 0x1p-7f;
+    stage_in<BITS, false, 0>(a.packed[d] + static_cast<size_t>(g0) * kIn, nvalid * kIn, area, lane, sl);
+    const float nscale = f16_value(a.norms[d][g0 + slot]) * 0x1p-7f;
     wait_vmem();
     uint32_t words[4 * BITS];
 #pragma unroll
@@ -964,45 +975,58 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     float v[kBlock];
     decode_stage1<BITS, kBlock>(words, pairs, v);
     fwht<kBlock, 2>(v);
-    // the bf16 values of the dequantised block, as fp32
+    // the group's bounds, taken on the fp32 values before their bf16
+    // rounding: rounding to nearest is monotone, so the rounded minimum is
+    // the minimum of the rounded values (likewise the maximum)
 #pragma unroll
-    for (int j = 0; j < kBlock; j += 2) {
-      const uint32_t pk = pack_bf16x2(v[j] * nscale, v[j + 1] * nscale);
-      v[j] = bf16_lo(pk);
-      v[j + 1] = bf16_hi(pk);
-    }
+    for (int j = 0; j < kBlock; ++j) v[j] = v[j] * nscale;
     float lo = 0.0f, hi = 0.0f;
 #pragma unroll
     for (int j = 0; j < kBlock; ++j) {
       lo = fminf(lo, v[j]);
       hi = fmaxf(hi, v[j]);
     }
+    {
+      const uint32_t lh = pack_bf16x2(lo, hi);
+      lo = bf16_lo(lh);
+      hi = bf16_hi(lh);
+    }
     float scale = (hi - lo) / 15.0f;
     scale = (scale == 0.0f) ? 1.0f : scale;
     const float inv = 1.0f / scale;
     const int32_t zp = static_cast<int32_t>(__builtin_fminf(__builtin_fmaxf(__builtin_rintf(-lo * inv), 0.0f), 15.0f));
-    const int32_t bias = zp - kRoundMagicBits;
+    // q = clamp(rint(RN(w * inv)) + zp, 0, 15): t = RN(RN(w * inv) + 1.5 2^23)
+    // is the integer rint(RN(w * inv)) + 1.5 2^23, exact in the binade
+    // [2^23, 2^24) where consecutive integers have consecutive bit patterns;
+    // clamped there to [B, B + 15], B = 1.5 2^23 - zp, its bits are bits(B) + q.
+    // The Horner steps acc = acc 16 + bits(t) then give, modulo 2^32, the
+    // nibbles plus bits(B) 0x11111111, taken off once per word.
+    const float qlo = kRoundMagic - static_cast<float>(zp), qhi = qlo + 15.0f;
+    const uint32_t excess = __float_as_uint(qlo) * 0x11111111u;
     uint32_t nib[16];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    for (int mw = 0; mw < 16; ++mw) {
+      uint32_t w2[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w2[k] = pack_bf16x2(v[8 * mw + 2 * k], v[8 * mw + 2 * k + 1]);
       uint32_t acc = 0;
 #pragma unroll
       for (int k = 7; k >= 0; --k) {
-        const int32_t r = static_cast<int32_t>(__float_as_uint(v[8 * m + k] * inv + kRoundMagic)) + bias;
-        const uint32_t q = static_cast<uint32_t>(r < 0 ? 0 : (r > 15 ? 15 : r));
-        acc = (acc << 4) | q;
+        const float w = (k & 1) ? bf16_hi(w2[k >> 1]) : bf16_lo(w2[k >> 1]);
+        const float t = __builtin_amdgcn_fmed3f(w * inv + kRoundMagic, qlo, qhi);
+        acc = (acc << 4) + __float_as_uint(t);
       }
-      nib[m] = acc;
+      nib[mw] = acc - excess;
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const u32x4 val = {nib[4 * q], nib[4 * q + 1], nib[4 * q + 2], nib[4 * q + 3]};
       *reinterpret_cast<u32x4*>(area + 64 * lane + 16 * q) = val;
     }
-    stage_out<4, false>(a.q4 + static_cast<size_t>(g0) * 64, nvalid * 64u, area, lane, sl);
+    stage_out<4, false>(a.q4[d] + static_cast<size_t>(g0) * 64, nvalid * 64u, area, lane, sl);
     if (static_cast<uint32_t>(lane) < nvalid) {
-      a.scales[g0 + lane] = scale;
-      a.zeros[g0 + lane] = static_cast<uint8_t>(zp);
+      a.scales[d][g0 + lane] = scale;
+      a.zeros[d][g0 + lane] = static_cast<uint8_t>(zp);
     }
   }
 }
@@ -1681,31 +1705,62 @@ int run_kv(bool quant, const void* kv, void* packed, void* norms, int64_t batch,
   return launch_kv(quant, bits, a, bh, stream);
 }
 
-int run_dequantize_int4(const void* packed, const void* norms, int64_t n_mats, int64_t out, int64_t in, int block,
-                        int bits, void* q4, void* scales, void* zeros, hipStream_t stream) {
-  if (block != kBlock) return HLWQ_ERR_BLOCK;
-  if (bits != 5 && bits != 3) return HLWQ_ERR_BITS;
-  if (n_mats < 0 || out < 0 || in < 0 || in % kBlock) return HLWQ_ERR_SHAPE;
-  int64_t rows, nblocks;
-  if (!mul_ok(n_mats, out, &rows) || !mul_ok(rows, in / kBlock, &nblocks)) return HLWQ_ERR_SHAPE;
-  if (nblocks == 0) return HLWQ_OK;
-  if (!packed || !norms || !q4 || !scales || !zeros) return HLWQ_ERR_NULL;
-  if (nblocks > 0x7fffffff - 64) return HLWQ_ERR_LIMIT;
-  if ((reinterpret_cast<uintptr_t>(packed) & 15u) || (reinterpret_cast<uintptr_t>(norms) & 1u) ||
-      (reinterpret_cast<uintptr_t>(q4) & 15u) || (reinterpret_cast<uintptr_t>(scales) & 3u))
+// Validate one INT4 descriptor; *blocks = rows * in / 128 (0: nothing to do).
+int check_int4_desc(const hlwq_int4_desc& m, int64_t* blocks) {
+  *blocks = 0;
+  if (m.rows < 0 || m.in < 0 || m.in % kBlock) return HLWQ_ERR_SHAPE;
+  int64_t nblk, bytes;
+  if (!mul_ok(m.rows, m.in / kBlock, &nblk) || !mul_ok(nblk, 80, &bytes)) return HLWQ_ERR_SHAPE;
+  if (nblk == 0) return HLWQ_OK;
+  if (!m.packed || !m.norms || !m.q4 || !m.scales || !m.zeros) return HLWQ_ERR_NULL;
+  if (nblk > 0x7fffffff - 64) return HLWQ_ERR_LIMIT;
+  if ((reinterpret_cast<uintptr_t>(m.packed) & 15u) || (reinterpret_cast<uintptr_t>(m.norms) & 1u) ||
+      (reinterpret_cast<uintptr_t>(m.q4) & 15u) || (reinterpret_cast<uintptr_t>(m.scales) & 3u))
     return HLWQ_ERR_ALIGN;
-  Int4Args a;
-  a.packed = static_cast<const uint8_t*>(packed);
-  a.norms = static_cast<const uint16_t*>(norms);
-  a.q4 = static_cast<uint8_t*>(q4);
-  a.scales = static_cast<float*>(scales);
-  a.zeros = static_cast<uint8_t*>(zeros);
-  a.nblocks = static_cast<uint32_t>(nblocks);
-  a.total_batches = static_cast<uint32_t>(ceil_div(nblocks, 64));
-  const dim3 grid(persistent_grid(a.total_batches)), block_dim(kThreads);
-  if (bits == 5) hipLaunchKernelGGL(hlwq_dequantize_int4_kernel<5>, grid, block_dim, 0, stream, a);
-  else hipLaunchKernelGGL(hlwq_dequantize_int4_kernel<3>, grid, block_dim, 0, stream, a);
-  return launch_status();
+  *blocks = nblk;
+  return HLWQ_OK;
+}
+
+int run_dequantize_int4(const hlwq_int4_desc* mats, int n, int bits, hipStream_t stream) {
+  if (n < 0) return HLWQ_ERR_SHAPE;
+  if (n > 0 && !mats) return HLWQ_ERR_NULL;
+  if (bits != 5 && bits != 3) return HLWQ_ERR_BITS;
+  for (int i = 0; i < n; ++i) {  // validate everything before enqueuing anything
+    int64_t b;
+    const int st = check_int4_desc(mats[i], &b);
+    if (st != HLWQ_OK) return st;
+  }
+  int i = 0;
+  while (i < n) {
+    Int4Group g;
+    std::memset(&g, 0, sizeof(g));
+    int64_t batches = 0;
+    for (; i < n && g.n < kMaxGroup; ++i) {
+      int64_t nblk;
+      check_int4_desc(mats[i], &nblk);
+      if (nblk == 0) continue;
+      // a matrix has fewer than 2^25 batches, so a launch always takes its first one
+      if (batches + ceil_div(nblk, 64) > 0xffffffffll) break;
+      const int k = g.n++;
+      g.batch_start[k] = static_cast<uint32_t>(batches);
+      g.nblocks[k] = static_cast<uint32_t>(nblk);
+      g.packed[k] = static_cast<const uint8_t*>(mats[i].packed);
+      g.norms[k] = static_cast<const uint16_t*>(mats[i].norms);
+      g.q4[k] = static_cast<uint8_t*>(mats[i].q4);
+      g.scales[k] = static_cast<float*>(mats[i].scales);
+      g.zeros[k] = static_cast<uint8_t*>(mats[i].zeros);
+      batches += ceil_div(nblk, 64);
+    }
+    if (g.n == 0) continue;
+    g.batch_start[g.n] = static_cast<uint32_t>(batches);
+    g.total_batches = static_cast<uint32_t>(batches);
+    const dim3 grid(persistent_grid(g.total_batches)), block_dim(kThreads);
+    if (bits == 5) hipLaunchKernelGGL(hlwq_dequantize_int4_kernel<5>, grid, block_dim, 0, stream, g);
+    else hipLaunchKernelGGL(hlwq_dequantize_int4_kernel<3>, grid, block_dim, 0, stream, g);
+    const int st = launch_status();
+    if (st != HLWQ_OK) return st;
+  }
+  return HLWQ_OK;
 }
 
 int run_kv_append(const void* src, int64_t batch, int64_t heads, int64_t n_new, int64_t tokens, void* ring,
@@ -1883,8 +1938,22 @@ int hlwq_kv_dequantize(const void* packed_u8, const void* norms_f16, int64_t bat
 
 int hlwq_dequantize_int4(const void* packed_u8, const void* norms_f16, int64_t n_mats, int64_t out, int64_t in,
                          int block, int bits, void* q4_u8, void* scales_f32, void* zeros_u8, void* hip_stream) {
-  return run_dequantize_int4(packed_u8, norms_f16, n_mats, out, in, block, bits, q4_u8, scales_f32, zeros_u8,
-                             static_cast<hipStream_t>(hip_stream));
+  if (block != kBlock) return HLWQ_ERR_BLOCK;
+  if (bits != 5 && bits != 3) return HLWQ_ERR_BITS;
+  if (n_mats < 0 || out < 0) return HLWQ_ERR_SHAPE;
+  hlwq_int4_desc m;
+  if (!mul_ok(n_mats, out, &m.rows)) return HLWQ_ERR_SHAPE;
+  m.packed = packed_u8;
+  m.norms = norms_f16;
+  m.q4 = q4_u8;
+  m.scales = scales_f32;
+  m.zeros = zeros_u8;
+  m.in = in;
+  return run_dequantize_int4(&m, 1, bits, static_cast<hipStream_t>(hip_stream));
+}
+
+int hlwq_dequantize_int4_grouped(const hlwq_int4_desc* mats, int n, int bits, void* hip_stream) {
+  return run_dequantize_int4(mats, n, bits, static_cast<hipStream_t>(hip_stream));
 }
 
 int hlwq_kv_append(const void* new_kv_bf16, int64_t batch, int64_t heads, int64_t n_new, int64_t tokens,
