@@ -395,7 +395,7 @@ __device__ __forceinline__ void fill_pairs(float* pairs, const float* __restrict
 // LDS staging
 //
 // Every wave owns a 16 KB slice of LDS.  Inputs reach it through direct
-// global->LDS loads (global_load_lds_dwordx4): in load instruction i, lane l
+// global->LDS loads (buffer_load_dwordx4 ... lds): in load instruction i, lane l
 // fills slot 64 i + l, so each instruction is one contiguous 1 KB of LDS and,
 // with the slot->chunk map below, one contiguous 1 KB of global memory too.
 // The map XORs the low 4 bits of a 16-byte chunk index with its 256-byte-row
@@ -448,33 +448,36 @@ __device__ __forceinline__ SwzLane swz_lane(int lane) {
   return sl;
 }
 
-// Stage `bytes` (<= 1024 * NI) of global memory starting at the 16-byte
-// aligned address src: chunk q (16 bytes) lands in slot swz(q) if SWZ, else q.
-// Chunks past `bytes` re-read src and are never consumed.  AUX is the cache
-// policy of the loads.
+// Stage `bytes` (<= 1024 * NI, a multiple of 16) of global memory starting
+// at the 16-byte aligned address src: chunk q (16 bytes) lands in slot swz(q)
+// if SWZ, else q.  The loads go through a buffer resource over exactly those
+// bytes, so chunks past the end read as zeros without a per-lane clamp (the
+// whole offset is in the VGPR operand, which is what the range check covers).
+// AUX is the cache policy of the loads.
 template <int NI, bool SWZ, int AUX>
 __device__ __forceinline__ void stage_in(const uint8_t* src, uint32_t bytes, uint8_t* stage, int lane,
                                          const SwzLane& sl) {
+  const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src), static_cast<short>(0),
+                                                   static_cast<int>(bytes), 0x00020000);
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const uint32_t off = 1024u * i + (SWZ ? sl.o[i & 3] : 16u * lane);
-    __builtin_amdgcn_global_load_lds(src + (off < bytes ? off : 0u), stage + 1024 * i, 16, 0, AUX);
-  }
+  for (int i = 0; i < NI; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(stage + 1024 * i), 16,
+                                             1024u * i + (SWZ ? sl.o[i & 3] : 16u * lane), 0, 0, AUX);
 }
 
-// Write back `bytes` of staged output (chunk q in slot swz(q) if SWZ) to dst
-// with 1 KB-contiguous stores.
+// Write back `bytes` (a multiple of 16) of staged output (chunk q in slot
+// swz(q) if SWZ) to dst with 1 KB-contiguous stores; through a buffer
+// resource over exactly those bytes, so the stores of chunks past the end are
+// dropped without a branch.
 template <int NI, bool SWZ>
 __device__ __forceinline__ void stage_out(uint8_t* dst, uint32_t bytes, const uint8_t* stage, int lane,
                                           const SwzLane& sl) {
+  const auto r = __builtin_amdgcn_make_buffer_rsrc(dst, static_cast<short>(0), static_cast<int>(bytes), 0x00020000);
   lds_handover();
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const uint32_t q = 64u * i + lane;
-    if (16u * q < bytes) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + 1024u * i + (SWZ ? sl.o[i & 3] : 16u * lane));
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + 16u * q));
-    }
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + 1024u * i + (SWZ ? sl.o[i & 3] : 16u * lane));
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, 1024u * i + 16u * lane, 0, kNt);
   }
   lds_handover();
 }
@@ -1047,6 +1050,28 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 // instruction is still one contiguous KB of HBM.  Stores use the same map.
 // ---------------------------------------------------------------------------
 
+// Division of a wave-uniform 32-bit numerator by a launch-invariant divisor
+// d >= 1 on the scalar unit (Granlund & Montgomery, "Division by invariant
+// integers using multiplication", PLDI 1994, section 4): with l = ceil(log2 d)
+// and m = floor(2^32 (2^l - d) / d) + 1, n / d = (t + ((n - t) >> s1)) >> s2
+// for t = mulhi(m, n), s1 = min(l, 1), s2 = max(l - 1, 0).
+struct UDiv {
+  uint32_t m, s1, s2;
+};
+UDiv make_udiv(uint32_t d) {
+  uint32_t l = 0;
+  while (l < 32 && (uint64_t{1} << l) < d) ++l;
+  UDiv v;
+  v.m = static_cast<uint32_t>(((uint64_t{1} << 32) * ((uint64_t{1} << l) - d)) / d + 1);
+  v.s1 = l < 1 ? l : 1;
+  v.s2 = l > 1 ? l - 1 : 0;
+  return v;
+}
+__device__ __forceinline__ uint32_t udiv(uint32_t n, const UDiv& v) {
+  const uint32_t t = __umulhi(v.m, n);
+  return (t + ((n - t) >> v.s1)) >> v.s2;
+}
+
 struct KvArgs {
   uint16_t* kv;       // [bh][tokens][256]
   uint8_t* packed;    // [bh][out_stride][32 * bits]
@@ -1056,6 +1081,7 @@ struct KvArgs {
   int64_t out_offset; // row of token 0 in packed / norms
   uint32_t tq;        // quantised tokens per head
   uint32_t nbt;       // batches per head, ceil(tq / 16)
+  UDiv nbt_div;       // division by nbt
   uint32_t total_batches;
   uint32_t chunk;      // batches per workgroup, 0 for a persistent grid (batch_range)
 };
@@ -1111,7 +1137,7 @@ struct KvBatch {
 };
 __device__ __forceinline__ KvBatch kv_batch(const KvArgs& a, uint32_t b) {
   KvBatch p;
-  p.bh = b / a.nbt;
+  p.bh = udiv(b, a.nbt_div);
   p.t0 = (b - p.bh * a.nbt) * kKvTokens;
   const uint32_t left = a.tq - p.t0;
   p.nvalid = left < kKvTokens ? left : kKvTokens;
@@ -1156,14 +1182,16 @@ __global__ void __launch_bounds__(kKvPoolThreads) __attribute__((amdgpu_waves_pe
     if (lane == 0) m_next = __hip_atomic_fetch_add(&next_batch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     asm volatile("" : "+v"(vsrc), "+v"(row_a));  // keep the address bases in one VGPR each
     const KvBatch p = kv_batch(a, b);
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv + (static_cast<int64_t>(p.bh) * a.tokens + p.t0) * kKvDim);
-    // chunks past a short batch reload its first chunk (lanes of missing tokens compute on it and store nothing)
-    const uint32_t bytes = p.nvalid * 2u * kKvDim;
+    const uint16_t* src = a.kv + (static_cast<int64_t>(p.bh) * a.tokens + p.t0) * kKvDim;
+    // a buffer resource over the batch's tokens: the chunks of a short
+    // batch's missing tokens lie past its end and read as zeros (their lanes
+    // compute on them and store nothing); the whole offset is in the VGPR
+    // operand, which is what the range check covers
+    const auto rs = batch_rsrc(src, p.nvalid * 2u * kKvDim);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t off = 1024u * k + vsrc;
-      __builtin_amdgcn_global_load_lds(src + (off < bytes ? off : 0u), stage + 1024 * k, 16, 0, kNt);
-    }
+    for (int k = 0; k < 8; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + 1024 * k), 16,
+                                               1024u * k + vsrc, 0, 0, kNt);
     wait_vmem();
     float x[64];
 #pragma unroll
@@ -1205,8 +1233,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
   // centroid pair table at offset 0 (512 bytes at most), then the per-wave stages
   constexpr uint32_t kVec = 32 * BITS;  // packed bytes per vector
   __shared__ __attribute__((aligned(256))) uint8_t lds[512 + kWaves * kKvStage];
-  fill_pairs<BITS>(reinterpret_cast<float*>(lds), (BITS == 3) ? c_cent3 : c_cent2);
-  __syncthreads();
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1219,14 +1245,31 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
   const float sgn1 = pair_sign(q & 1u), sgn2 = pair_sign(q & 2u);
   const SwzLane linear{};
 
-  const BatchRange br = batch_range(a.total_batches, a.chunk, wave);
-  for (uint32_t b = br.b; b < br.end; b += br.step) {
+  // Codes and norm of batch b: the codes go to the stage, the norm to `n16`.
+  // A workgroup is short-lived (one batch per wave at the usual chunk), so the
+  // first batch's are requested before the pair table is built and the table
+  // fill runs while they are in flight.  (The longer-lived weight dequantizer
+  // and the KV quantizer measured slower with the same change.)
+  KvBatch p{};
+  size_t vec0 = 0;
+  uint32_t vv = 0;
+  uint16_t n16 = 0;
+  auto request = [&](uint32_t bb) {
     asm volatile("" : "+v"(vsrc), "+v"(stage_a));
-    const KvBatch p = kv_batch(a, b);
-    const uint32_t vv = v < p.nvalid ? v : p.nvalid - 1u;  // lanes past the end repeat the last token
-    const size_t vec0 = static_cast<size_t>(p.bh) * a.out_stride + a.out_offset + p.t0;
+    p = kv_batch(a, bb);
+    vv = v < p.nvalid ? v : p.nvalid - 1u;  // lanes past the end repeat the last token
+    vec0 = static_cast<size_t>(p.bh) * a.out_stride + a.out_offset + p.t0;
     stage_in<2, false, 0>(a.packed + vec0 * kVec, p.nvalid * kVec, stage, lane, linear);
-    const float scale = f16_value(a.norms[vec0 + vv]) * 0x1p-8f;
+    n16 = a.norms[vec0 + vv];
+  };
+  const BatchRange br = batch_range(a.total_batches, a.chunk, wave);
+  if (br.b < br.end) request(br.b);
+  fill_pairs<BITS>(reinterpret_cast<float*>(lds), (BITS == 3) ? c_cent3 : c_cent2);
+  __syncthreads();
+
+  for (uint32_t b = br.b; b < br.end; b += br.step) {
+    if (b != br.b) request(b);
+    const float scale = f16_value(n16) * 0x1p-8f;
     wait_vmem();
     uint32_t words[2 * BITS];
     const uint32_t lo = kVec * vv + 8u * BITS * q;
@@ -1263,14 +1306,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
       lds_write16(stage_a + 128u * ul + 16u * (static_cast<uint32_t>(c) ^ (ul & 7u)),
                   u32x4{pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]});
     lds_handover();
-    uint8_t* dst = reinterpret_cast<uint8_t*>(a.kv + (static_cast<int64_t>(p.bh) * a.tokens + p.t0) * kKvDim);
-    const uint32_t bytes = p.nvalid * 2u * kKvDim;
+    // stores through a buffer resource over the batch's tokens: those of
+    // missing tokens lie past its end and are dropped
+    const auto rd = batch_rsrc(a.kv + (static_cast<int64_t>(p.bh) * a.tokens + p.t0) * kKvDim, p.nvalid * 2u * kKvDim);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const u32x4 val = lds_read16(stage_a + 1024u * k + 16u * ul);
-      const uint32_t off = 1024u * k + vsrc;
-      if (off < bytes) __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(dst + off));
-    }
+    for (int k = 0; k < 8; ++k)
+      __builtin_amdgcn_raw_buffer_store_b128(lds_read16(stage_a + 1024u * k + 16u * ul), rd, 1024u * k + vsrc, 0, kNt);
     lds_handover();
   }
 }
@@ -1647,6 +1688,8 @@ int make_single(const void* w, const void* packed, const void* norms, int64_t n_
 // heads per launch, at most kMaxDispatch workgroups' worth of batches each.
 int launch_kv(bool quant, int bits, KvArgs a, int64_t bh, hipStream_t stream) {
   a.nbt = static_cast<uint32_t>(ceil_div(a.tq, kKvTokens));
+  if (a.nbt == 0 || bh == 0) return HLWQ_OK;
+  a.nbt_div = make_udiv(a.nbt);
   // quantize: one 16-wave workgroup per CU drawing from its work pool (5%
   // faster than a fixed share per wave on a 2 x 4-head cache of 32768
   // tokens); dequantize: one batch per wave, workgroups handed out by the
