@@ -127,6 +127,74 @@ def test_unaligned_rows(wq):
         assert bf16_bits(outbuf[:1])[0] == 0
 
 
+def test_ragged_batches_touch_nothing_past_the_end(wq):
+    # The last batch of a matrix is short, and rows of a tail-block matrix end
+    # mid-batch: the staged loads must not pick up the bytes that follow the
+    # input (NaN here), and the staged stores must not write past the outputs
+    # (sentinels here), for quantize, dequantize and dequantize -> INT4.
+    nan = 0x7FC0
+    for rows, n_in in ((37, 256), (33, 704), (130, 1000), (5, 128)):
+        nb = -(-n_in // 128)
+        w_bits = synth.random_bf16((rows, n_in), seed=rows + n_in)
+        base = torch.full(((rows + 9) * n_in,), float("nan"), dtype=torch.bfloat16, device="cuda")
+        base[:rows * n_in] = to_dev(w_bits).reshape(-1)
+        w = base[:rows * n_in].view(rows, n_in)
+        pbuf = torch.full(((rows + 2) * nb * 80,), 0xA5, dtype=torch.uint8, device="cuda")
+        nbuf = torch.full(((rows + 2) * nb,), -1.5, dtype=torch.float16, device="cuda")
+        packed = pbuf[:rows * nb * 80].view(rows, nb, 80)
+        norms = nbuf[:rows * nb].view(rows, nb)
+        wq.hlwq_quantize(w, 5, packed=packed, norms=norms)
+        obuf = torch.full(((rows + 3) * n_in,), -2.0, dtype=torch.bfloat16, device="cuda")
+        out = obuf[:rows * n_in].view(rows, n_in)
+        wq.hlwq_dequantize(packed, norms, n_in, 5, out=out)
+        torch.cuda.synchronize()
+        assert not np.any(bf16_bits(base[rows * n_in:]) != nan)
+        op, on = ref.quantize_c(w_bits, 5)
+        assert np.array_equal(packed.cpu().numpy(), op), (rows, n_in)
+        assert np.array_equal(f16_bits(norms), on.view(np.uint16)), (rows, n_in)
+        assert np.all(pbuf[rows * nb * 80:].cpu().numpy() == 0xA5), (rows, n_in)
+        assert np.all(f16_bits(nbuf[rows * nb:]) == np.float16(-1.5).view(np.uint16)), (rows, n_in)
+        assert np.array_equal(bf16_bits(out), ref.dequantize_c(op, on, n_in, 5)), (rows, n_in)
+        assert np.all(bf16_bits(obuf[rows * n_in:]) == 0xC000), (rows, n_in)  # -2.0
+        if n_in % 128 == 0:
+            q4buf = torch.full(((rows + 2) * n_in // 2,), 0x5A, dtype=torch.uint8, device="cuda")
+            q4 = q4buf[:rows * n_in // 2].view(rows, n_in // 2)
+            _, sc, z = wq.hlwq_dequantize_int4(packed, norms, n_in, 5, q4=q4)
+            torch.cuda.synchronize()
+            eq, es, ez = ref.dequantize_to_int4_c(op, on, n_in, 5)
+            assert np.array_equal(q4.cpu().numpy(), eq), (rows, n_in)
+            assert np.array_equal(sc.cpu().numpy().view(np.uint32), es.view(np.uint32)), (rows, n_in)
+            assert np.array_equal(z.cpu().numpy(), ez), (rows, n_in)
+            assert np.all(q4buf[rows * n_in // 2:].cpu().numpy() == 0x5A), (rows, n_in)
+    # KV: a token count whose last 16-token batch is short; with no window,
+    # that batch's missing tokens lie past the cache, where NaN follows; the
+    # outputs are followed by sentinels
+    B, H, T = 1, 2, 128 + 37
+    kv_bits = synth.random_bf16((B, H, T, 256), seed=11, sigma=1.0)
+    kbuf = torch.full((B * H * T * 256 + 4096,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kbuf[:B * H * T * 256] = to_dev(kv_bits).reshape(-1)
+    kv = kbuf[:B * H * T * 256].view(B, H, T, 256)
+    for bits, n_res in ((3, 128), (2, 0), (3, 0)):
+        tq = T - n_res
+        pk = torch.full(((B * H * tq + 3) * 32 * bits,), 0xA5, dtype=torch.uint8, device="cuda")
+        nk = torch.full((B * H * tq + 3,), -1.5, dtype=torch.float16, device="cuda")
+        p = pk[:B * H * tq * 32 * bits].view(B, H, tq, 32 * bits)
+        n = nk[:B * H * tq].view(B, H, tq)
+        wq.hlwq_kv_quantize(kv, n_residual=n_res, bits=bits, packed=p, norms=n)
+        dbuf = torch.full((B * H * T * 256 + 4096,), -2.0, dtype=torch.bfloat16, device="cuda")
+        dk = dbuf[:B * H * T * 256].view(B, H, T, 256)
+        wq.hlwq_kv_dequantize(p, n, dk, n_residual=n_res, bits=bits)
+        torch.cuda.synchronize()
+        op, on = ref.kv_quantize_c(kv_bits, n_residual=n_res, bits=bits)
+        assert np.array_equal(p.cpu().numpy(), op), (bits, n_res)
+        assert np.array_equal(f16_bits(n), on.view(np.uint16)), (bits, n_res)
+        assert np.all(pk[B * H * tq * 32 * bits:].cpu().numpy() == 0xA5), (bits, n_res)
+        assert np.all(f16_bits(nk[B * H * tq:]) == np.float16(-1.5).view(np.uint16)), (bits, n_res)
+        assert np.array_equal(bf16_bits(dk)[:, :, :tq], ref.kv_dequantize_c(op, on, bits=bits)), (bits, n_res)
+        assert np.all(bf16_bits(dk)[:, :, tq:] == 0xC000), (bits, n_res)  # the window rows: -2.0, untouched
+        assert np.all(bf16_bits(dbuf[B * H * T * 256:]) == 0xC000), (bits, n_res)
+
+
 def _special_rows():
     f = synth.f32_to_bf16_bits
     rows = []
