@@ -119,6 +119,28 @@ def stored_traffic(config, bits):
         return None
 
 
+def stored_valu(config, bits):
+    """VALU instructions per weight (SQ_INSTS_VALU x 64 lanes / weights) of
+    the quantize and dequantize kernels from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"counters_{config}_q{bits}.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        for key in ("kernel_source_sha256_16", "valu_ops_per_value_quantize", "valu_ops_per_value_dequantize"):
+            if line.startswith(key + ":"):
+                vals[key] = line.split(":", 1)[1].strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return {"quantize": float(vals["valu_ops_per_value_quantize"]),
+                "dequantize": float(vals["valu_ops_per_value_dequantize"]),
+                "source": os.path.relpath(path, ROOT)}
+    except (KeyError, ValueError):
+        return None
+
+
 # Working sets below this many bytes are held in two copies, and dequantize
 # reads the copy that quantize did not just write, so its input comes from HBM
 # and not from the 256 MB memory-side cache.
@@ -706,6 +728,8 @@ def extra_bank(torch, wq, dev, ceil, config, bits, steps, warmup):
            "settle": {"seconds": SETTLE_S, "steps": n_settle},
            "quantize": leg(q_ms, nbytes, weights, c["quantize_mix"]),
            "dequantize": leg(d_ms, nbytes, weights, c["dequantize_mix"]),
+           "traffic": stored_traffic(config, bits),
+           "valu_ops_per_value": stored_valu(config, bits),
            "ceiling": c}
     del wl
     torch.cuda.empty_cache()
@@ -828,6 +852,9 @@ def main():
         "quantize": leg(q_ms, bytes_dir, weights, ceiling["quantize_mix"]),
         "dequantize": leg(d_ms, bytes_d, weights, ceiling["dequantize_mix"]),
         "roofline": roofline,
+        # VALU instructions per quantised value from the committed counters
+        # (null when they were taken on other kernel source)
+        "valu_ops_per_value": stored_valu(config, bits) if args.layout == "packed" else None,
         "ceiling": ceiling,
     }
     del wl

@@ -25,3 +25,28 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert r.returncode != 0
     assert "one GPU" in r.stderr or "--gpus 1" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_committed_counters_are_read_only_for_the_current_kernel_source(tmp_path, monkeypatch):
+    # traffic and VALU counts come from the committed rocprofv3 summaries, and
+    # only while the kernel source they were taken on is unchanged
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "hbm_traffic_x_q5.txt").write_text(
+        "# comment: ignored\nkernel_source_sha256_16: %s\nquantize_bytes_per_launch: 100\n"
+        "dequantize_bytes_per_launch: 200\n" % bench.kernel_source_hash())
+    (prof / "counters_x_q5.md").write_text(
+        "# Instruction counters\n\nCommands (MI355X, one GPU):\n\nkernel_source_sha256_16: %s\n"
+        "valu_ops_per_value_quantize: 15.06\nvalu_ops_per_value_dequantize: 8.97\n" % bench.kernel_source_hash())
+    (prof / "counters_y_q5.md").write_text(
+        "kernel_source_sha256_16: 0000000000000000\nvalu_ops_per_value_quantize: 1\nvalu_ops_per_value_dequantize: 2\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: open(prof / "counters_x_q5.md").read().split(
+        "kernel_source_sha256_16: ")[1][:16])
+    assert bench.stored_traffic("x", 5) == {"quantize_bytes_per_launch": 100.0, "dequantize_bytes_per_launch": 200.0}
+    v = bench.stored_valu("x", 5)
+    assert v["quantize"] == 15.06 and v["dequantize"] == 8.97
+    assert bench.stored_valu("y", 5) is None          # taken on other source
+    assert bench.stored_valu("z", 5) is None          # no summary
+    assert bench.stored_traffic("z", 5) is None
+
