@@ -339,6 +339,30 @@ def test_kv_cache_small(wq, shape):
     assert np.all(got[:, :, tq:] == 0x3F80), "residual window must stay untouched"
 
 
+@pytest.mark.parametrize("nbt", [1, 2, 3, 5, 7, 64, 333])
+def test_kv_batches_per_head(wq, nbt):
+    # the kernels map a batch index to (head, first token) by dividing by the
+    # batches per head on the scalar unit: head counts and token counts that
+    # give every residue, a short last batch per head and power-of-two and
+    # odd divisors
+    B, H = 1, 9
+    T = 128 + 16 * nbt - (3 if nbt > 1 else 0)
+    kv = synth.random_bf16((B, H, T, 256), seed=1000 + nbt, sigma=1.0)
+    _say("kv batches per head", nbt, T)
+    dev = to_dev(kv)
+    packed, norms = wq.hlwq_kv_quantize(dev, n_residual=128)
+    out = to_dev(np.full((B, H, T, 256), 0x3F80, np.uint16))
+    wq.hlwq_kv_dequantize(packed, norms, out, n_residual=128)
+    torch.cuda.synchronize()
+    op, on = ref.kv_quantize_c(kv, n_residual=128)
+    assert np.array_equal(packed.cpu().numpy(), op)
+    assert np.array_equal(f16_bits(norms), on.view(np.uint16))
+    tq = T - 128
+    got = bf16_bits(out)
+    assert np.array_equal(got[:, :, :tq], ref.kv_dequantize_c(op, on))
+    assert np.all(got[:, :, tq:] == 0x3F80)
+
+
 @pytest.mark.parametrize("shape", [(1, 2, 300), (2, 3, 129), (1, 1, 1000)])
 def test_kv_cache_q2(wq, shape):
     B, H, T = shape
