@@ -873,6 +873,33 @@ def test_definition_tier_tail_blocks(wq):
     _bank_tier_d(wq, "gemma4_moe_bank", "down", 5, "Q5 Gemma-4 down bank (in=704, tail blocks)")
 
 
+@pytest.mark.parametrize("bits", [5, 3])
+def test_definition_tier_dense_student_t(wq, bits):
+    # every block of the three dense hidden-5120 Linears (Student-t(5) values,
+    # heavy tails: 205M weights)
+    t = TierD(f"Q{bits} dense 5120 Linears (Student-t)", bits)
+    for name in synth.CONFIGS["dense_5120"]:
+        wb = synth.weight("dense_5120", name)
+        rows, n_in = wb.shape
+        w = to_dev(wb)
+        packed, norms = wq.hlwq_quantize(w, bits)
+        out = wq.hlwq_dequantize(packed, norms, n_in, bits)
+        torch.cuda.synchronize()
+        gp, gn, go = packed.cpu().numpy(), f16_bits(norms).view(np.float16), bf16_bits(out)
+        del w, packed, norms, out
+        nb = n_in // 128
+
+        def job(rc):
+            r0, r1 = rc
+            x, _ = ref.blocks_from_rows(wb[r0:r1])
+            og = ref.bf16_to_f32(go[r0:r1]).reshape(r1 - r0, nb, 128)
+            return t.chunk(x.astype(np.float64), ref.unpack_codes(gp[r0:r1], bits), gn[r0:r1], og)
+
+        for r in host_map(job, _row_chunks(rows)):
+            t.add(r)
+    t.report_and_check()
+
+
 @pytest.mark.parametrize("bits", [3, 2])
 def test_definition_tier_kv_h256(wq, bits):
     # every quantised vector of the benchmark's K and V cache (66.8M values)
