@@ -41,8 +41,8 @@
  * Ownership and execution: the caller allocates every buffer, in device
  * memory of the current HIP device.  The library keeps no state beyond
  * constant tables compiled into the code object and each device's compute-unit
- * count (read once, kept in an atomic), and allocates nothing.  Every
- * call validates its arguments on the host first; on success it enqueues the
+ * count (read once, kept in an atomic), and allocates no device memory.
+ * Every call validates its arguments on the host first; on success it enqueues the
  * work on `hip_stream` (a hipStream_t; NULL means the default stream) and
  * returns without synchronising.  Calls are reentrant; calls on different
  * streams may run concurrently.
@@ -55,6 +55,13 @@
  * token count equal to 0) is valid, does nothing and accepts NULL pointers.
  * Inputs must be finite; a block whose squared norm overflows fp32 (an entry
  * above ~1.8e19 in magnitude) yields an infinite norm and unspecified codes.
+ *
+ * Overlap: a buffer a call writes may share no byte with any other buffer of
+ * the same call (every buffer taken at its whole extent, e.g. the full
+ * [B, H, T, 256] KV tensor even where only rows t < T - n_residual are
+ * written); such a call returns HLWQ_ERR_OVERLAP.  Buffers a call only reads
+ * may overlap each other.  Calls in flight on different streams are not
+ * checked against each other.
  *
  * Alignment: `packed` and KV-cache buffers must be 16-byte aligned, `norms`
  * and weight buffers 2-byte aligned.  Weight matrices whose rows do not all
@@ -79,8 +86,9 @@ enum {
   HLWQ_ERR_BLOCK = -4,   /* block != 128 (weights) or head_dim != 256 (KV) */
   HLWQ_ERR_DEVICE = -5,  /* the HIP launch reported an error */
   HLWQ_ERR_ALIGN = -6,   /* a buffer violates the alignment stated above */
-  HLWQ_ERR_LIMIT = -7    /* more than 2^31 - 1 blocks / vectors in one matrix or cache, or an append
+  HLWQ_ERR_LIMIT = -7,   /* more than 2^31 - 1 blocks / vectors in one matrix or cache, or an append
                             whose launch would exceed 2^32 - 1 work-items (about 6.7e7 heads) */
+  HLWQ_ERR_OVERLAP = -8  /* a buffer the call writes overlaps another buffer of the call */
 };
 
 /* One matrix of a grouped call.  For hlwq_quantize_grouped `w` is read and

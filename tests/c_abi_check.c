@@ -117,6 +117,15 @@ int main(void) {
   CHECK(hlwq_kv_append(buf, 1, 4, 0, 200, buf, 128, buf, buf, 300, 256, 3, NULL) == HLWQ_OK); /* nothing new */
   CHECK(hlwq_kv_append(buf, 1, 4, 1, 200, buf, 128, buf, buf, 50, 256, 3, NULL) == HLWQ_ERR_SHAPE); /* capacity */
   CHECK(hlwq_kv_append(NULL, 1, 4, 1, 200, buf, 128, buf, buf, 300, 256, 3, NULL) == HLWQ_ERR_NULL);
+  /* a call writing over one of its own buffers is refused (16-byte aligned
+     addresses inside a host array; nothing is dereferenced) */
+  {
+    char raw[256];
+    char* a16 = raw + ((16u - ((uintptr_t)raw & 15u)) & 15u);
+    CHECK(hlwq_quantize(a16, 1, 1, 8, 128, 5, a16, a16 + 128, NULL) == HLWQ_ERR_OVERLAP);
+    CHECK(hlwq_dequantize(a16, a16 + 128, 1, 1, 8, 128, 5, a16 + 64, NULL) == HLWQ_ERR_OVERLAP);
+    CHECK(strlen(hlwq_status_string(HLWQ_ERR_OVERLAP)) > 0);
+  }
   /* search tables: a partial copy of the bucket bytes, every entry, the constants */
   {
     uint8_t bytes[16];

@@ -14,7 +14,7 @@ from oracle import hlwq_ref as ref
 from oracle import lloyd_max as lm
 from oracle import tq3_ref as tq
 
-OK, ENULL, ESHAPE, EBITS, EBLOCK, EDEV, EALIGN, ELIMIT = 0, -1, -2, -3, -4, -5, -6, -7
+OK, ENULL, ESHAPE, EBITS, EBLOCK, EDEV, EALIGN, ELIMIT, EOVERLAP = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
 
 @pytest.fixture(scope="module")
@@ -91,7 +91,7 @@ def test_size_helpers():
 
 
 def test_status_strings(lib):
-    for st in (OK, ENULL, ESHAPE, EBITS, EBLOCK, EDEV, EALIGN, ELIMIT):
+    for st in (OK, ENULL, ESHAPE, EBITS, EBLOCK, EDEV, EALIGN, ELIMIT, EOVERLAP):
         assert wq.hlwq_status_string(st) != "unknown status"
     assert wq.hlwq_status_string(12345) == "unknown status"
 
@@ -212,6 +212,47 @@ def test_codes8_argument_errors(lib):
     assert d(A, None, 1, 4, 128, 128, 5, A, None) == ENULL
     assert d(A, A, 1, 4, 128, 128, 6, A, None) == EBITS
     assert d(A, A, 1, -4, 128, 128, 5, A, None) == ESHAPE
+
+
+def test_overlapping_buffers_are_refused(lib):
+    # Every call below would write a buffer that shares bytes with another of
+    # its buffers; each must be refused before anything is launched.  (Calls
+    # whose buffers are disjoint would launch, so they are exercised on the
+    # GPU with real tensors, not here.)
+    A = 0x100000
+    q, d = lib.hlwq_quantize, lib.hlwq_dequantize
+    # 4 x 128 bf16 = 1024 bytes of W; 4 blocks: 320 bytes of Q5 codes, 8 of norms
+    assert q(A, 1, 4, 128, 128, 5, A + 1008, A + 4096, None) == EOVERLAP   # codes over W's last 16 bytes
+    assert q(A, 1, 4, 128, 128, 5, A + 4096, A + 1022, None) == EOVERLAP   # norms over W's last 2 bytes
+    assert q(A + 16, 1, 4, 128, 128, 5, A, A + 4096, None) == EOVERLAP     # codes over W's first bytes
+    assert q(A, 1, 4, 128, 128, 5, A + 4096, A + 4096 + 318, None) == EOVERLAP  # norms over the codes
+    assert q(A, 1, 4, 128, 128, 5, A, A + 4096, None) == EOVERLAP          # in place
+    assert d(A + 4096, A + 8192, 1, 4, 128, 128, 5, A + 4096 - 16, None) == EOVERLAP  # out over the codes
+    assert d(A + 4096, A + 8192, 1, 4, 128, 128, 5, A + 7200, None) == EOVERLAP       # out over the norms
+    assert lib.hlwq_quantize_codes8(A, 1, 4, 128, 128, 5, A + 4096, A + 4096 + 510, None) == EOVERLAP
+    assert lib.hlwq_tq3_quantize(A, 1, 4, 128, 128, 42, A + 4096, A + 4096 + 188, None) == EOVERLAP
+    # grouped: one matrix's output over another matrix's input
+    descs = (wq.MatDesc * 2)()
+    descs[0] = wq.MatDesc(A, A + 8192, A + 12288, 4, 128)
+    descs[1] = wq.MatDesc(A + 16384, A + 512, A + 20480, 4, 128)
+    assert lib.hlwq_quantize_grouped(descs, 2, 5, None) == EOVERLAP
+    # grouped dequantize: two matrices written to overlapping outputs
+    descs[1] = wq.MatDesc(A + 512, A + 24576, A + 28672, 4, 128)
+    assert lib.hlwq_dequantize_grouped(descs, 2, 5, None) == EOVERLAP
+    # KV [1, 4, 300, 256]: 614,400 bytes of bf16; 172 quantised tokens per head
+    kq, kd = lib.hlwq_kv_quantize, lib.hlwq_kv_dequantize
+    B = A + (1 << 20)
+    assert kq(A, 1, 4, 300, 256, 3, 128, A + 614400 - 16, B, None) == EOVERLAP
+    assert kq(A, 1, 4, 300, 256, 3, 128, B, B + 688 * 96 - 2, None) == EOVERLAP
+    assert kd(B, B + (1 << 20), 1, 4, 300, 256, 3, 128, B - 614400 + 16, None) == EOVERLAP
+    # append: the window over the new tokens, the codes over the norms
+    ap = lib.hlwq_kv_append
+    assert ap(A, 1, 4, 1, 500, A + 2048 - 16, 128, B, B + (1 << 16), 400, 256, 3, None) == EOVERLAP
+    assert ap(A, 1, 4, 1, 500, A + 4096, 128, B, B + 1600 * 96 - 2, 400, 256, 3, None) == EOVERLAP
+    # INT4 [4, 256]: 8 blocks; q4 512 bytes, scales 32, zeros 8
+    d4 = lib.hlwq_dequantize_int4
+    assert d4(A, A + 4096, 1, 4, 256, 128, 5, A + 640 - 16, A + 8192, A + 12288, None) == EOVERLAP
+    assert d4(A, A + 4096, 1, 4, 256, 128, 5, A + 16384, A + 8192, A + 8192 + 28, None) == EOVERLAP
 
 
 @pytest.mark.parametrize("seed", [0, 1, 42, 1234567, 2 ** 64 - 1])

@@ -320,6 +320,124 @@ def test_non_default_stream_and_determinism(wq):
     assert np.array_equal(p1.cpu().numpy(), op)
 
 
+def _carve(buf, offset, nbytes, dtype, shape):
+    """A view of nbytes of the uint8 buffer at offset, as dtype / shape."""
+    offset, nbytes = int(offset), int(nbytes)
+    return buf[offset:offset + nbytes].view(dtype).view(shape)
+
+
+def test_buffers_back_to_back_in_one_allocation(wq):
+    # Inputs and outputs that touch (each starts where the previous one ends)
+    # are distinct buffers and must be accepted; so must one input shared by
+    # two matrices of a grouped call.  Every result is checked bit for bit.
+    rows, n_in = 64, 704  # tail blocks: 6 blocks per row, 384 blocks
+    wb = synth.random_bf16((rows, n_in), seed=55, outlier_frac=0.001, outlier_mult=20.0)
+    nblk = rows * 6
+    sizes = [rows * n_in * 2, nblk * 80, nblk * 2, rows * n_in * 2]
+    offs = np.cumsum([0] + sizes)
+    buf = torch.zeros(int(offs[-1]), dtype=torch.uint8, device="cuda")
+    w = _carve(buf, offs[0], sizes[0], torch.bfloat16, (rows, n_in))
+    packed = _carve(buf, offs[1], sizes[1], torch.uint8, (rows, 6, 80))
+    norms = _carve(buf, offs[2], sizes[2], torch.float16, (rows, 6))
+    out = _carve(buf, offs[3], sizes[3], torch.bfloat16, (rows, n_in))
+    w.copy_(to_dev(wb))
+    wq.hlwq_quantize(w, 5, packed=packed, norms=norms)
+    wq.hlwq_dequantize(packed, norms, n_in, 5, out=out)
+    torch.cuda.synchronize()
+    op, on = ref.quantize_c(wb, 5)
+    assert np.array_equal(packed.cpu().numpy(), op) and np.array_equal(f16_bits(norms), on.view(np.uint16))
+    assert np.array_equal(bf16_bits(out), ref.dequantize_c(op, on, n_in, 5))
+    assert np.array_equal(bf16_bits(w), wb), "the input must stay as it was"
+
+    # one W read by both matrices of a grouped call
+    p2, n2 = torch.empty_like(packed), torch.empty_like(norms)
+    p3, n3 = torch.empty_like(packed), torch.empty_like(norms)
+    wq.hlwq_quantize_grouped([(w, p2, n2), (w, p3, n3)], 5)
+    torch.cuda.synchronize()
+    for p_, n_ in ((p2, n2), (p3, n3)):
+        assert np.array_equal(p_.cpu().numpy(), op) and np.array_equal(f16_bits(n_), on.view(np.uint16))
+
+    # KV cache, codes and norms back to back; dequantized into the cache itself
+    B, H, T = 1, 3, 300
+    kvb = synth.random_bf16((B, H, T, 256), seed=56, sigma=1.0)
+    tq = T - 128
+    ks = [B * H * T * 512, B * H * tq * 96, B * H * tq * 2]
+    ko = np.cumsum([0] + ks)
+    kbuf = torch.zeros(int(ko[-1]), dtype=torch.uint8, device="cuda")
+    kv = _carve(kbuf, ko[0], ks[0], torch.bfloat16, (B, H, T, 256))
+    kp = _carve(kbuf, ko[1], ks[1], torch.uint8, (B, H, tq, 96))
+    kn = _carve(kbuf, ko[2], ks[2], torch.float16, (B, H, tq))
+    kv.copy_(to_dev(kvb))
+    wq.hlwq_kv_quantize(kv, n_residual=128, packed=kp, norms=kn)
+    wq.hlwq_kv_dequantize(kp, kn, kv, n_residual=128)
+    torch.cuda.synchronize()
+    okp, okn = ref.kv_quantize_c(kvb, n_residual=128)
+    assert np.array_equal(kp.cpu().numpy(), okp) and np.array_equal(f16_bits(kn), okn.view(np.uint16))
+    got = bf16_bits(kv)
+    assert np.array_equal(got[:, :, :tq], ref.kv_dequantize_c(okp, okn))
+    assert np.array_equal(got[:, :, tq:], kvb[:, :, tq:])
+
+    # INT4 outputs back to back after their inputs
+    n4 = 512
+    w4 = synth.random_bf16((rows, n4), seed=57)
+    op4, on4 = ref.quantize_c(w4, 5)
+    nb4 = rows * 4
+    s4 = [nb4 * 80, nb4 * 2, rows * n4 // 2, nb4 * 4, nb4]
+    o4 = np.cumsum([0] + s4)
+    ibuf = torch.zeros(int(o4[-1]), dtype=torch.uint8, device="cuda")
+    ip = _carve(ibuf, o4[0], s4[0], torch.uint8, (rows, 4, 80))
+    inn = _carve(ibuf, o4[1], s4[1], torch.float16, (rows, 4))
+    q4 = _carve(ibuf, o4[2], s4[2], torch.uint8, (rows, n4 // 2))
+    sc = _carve(ibuf, o4[3], s4[3], torch.float32, (rows, 4))
+    zp = _carve(ibuf, o4[4], s4[4], torch.uint8, (rows, 4))
+    ip.copy_(torch.from_numpy(op4).cuda())
+    inn.copy_(torch.from_numpy(on4.view(np.int16)).view(torch.float16).cuda())
+    wq.hlwq_dequantize_int4(ip, inn, n4, 5, q4=q4, scales=sc, zeros=zp)
+    torch.cuda.synchronize()
+    e4, es, ez = ref.dequantize_to_int4_c(op4, on4, n4, 5)
+    assert np.array_equal(q4.cpu().numpy(), e4)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), es.view(np.uint32))
+    assert np.array_equal(zp.cpu().numpy(), ez)
+
+
+def test_in_place_calls_are_refused(wq):
+    # a call whose output overlaps another of its buffers is refused on the
+    # host (status -8, nothing launched) and leaves every byte as it was
+    rows, n_in = 16, 256
+    wb = synth.random_bf16((rows, n_in), seed=58)
+    wbytes = rows * n_in * 2
+    buf = torch.zeros(wbytes + 8192, dtype=torch.uint8, device="cuda")
+    w = _carve(buf, 0, wbytes, torch.bfloat16, (rows, n_in))
+    w.copy_(to_dev(wb))
+    good_p, good_n = wq.hlwq_quantize(w, 5)
+    torch.cuda.synchronize()
+    before = buf.clone()
+
+    def refused(call):
+        with pytest.raises(wq.HLWQError) as e:
+            call()
+        assert e.value.status == -8
+        torch.cuda.synchronize()
+        assert torch.equal(buf, before)
+
+    # codes over the last KB of W; norms over W's last bytes
+    refused(lambda: wq.hlwq_quantize(w, 5, packed=_carve(buf, wbytes - 1024, rows * 160, torch.uint8, (rows, 2, 80)),
+                                     norms=torch.empty((rows, 2), dtype=torch.float16, device="cuda")))
+    refused(lambda: wq.hlwq_quantize(w, 5, packed=torch.empty((rows, 2, 80), dtype=torch.uint8, device="cuda"),
+                                     norms=_carve(buf, wbytes - 2, rows * 4, torch.float16, (rows, 2))))
+    # dequantize into a region that covers its own codes
+    codes = _carve(buf, wbytes, rows * 160, torch.uint8, (rows, 2, 80))
+    codes.copy_(good_p)
+    before = buf.clone()
+    refused(lambda: wq.hlwq_dequantize(codes, good_n, n_in, 5, out=_carve(buf, 4096, wbytes, torch.bfloat16,
+                                                                            (rows, n_in))))
+    # a KV cache dequantized over its own codes
+    kv = _carve(buf, 0, 1 * 1 * 16 * 512, torch.bfloat16, (1, 1, 16, 256))
+    refused(lambda: wq.hlwq_kv_dequantize(_carve(buf, 4096, 8 * 96, torch.uint8, (1, 1, 8, 96)),
+                                          torch.empty((1, 1, 8), dtype=torch.float16, device="cuda"), kv,
+                                          n_residual=8))
+
+
 @pytest.mark.parametrize("shape", [(1, 2, 300), (2, 3, 1000), (1, 1, 129), (1, 4, 128), (1, 1, 5)])
 def test_kv_cache_small(wq, shape):
     B, H, T = shape

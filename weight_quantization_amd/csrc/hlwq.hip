@@ -33,10 +33,12 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cfloat>
 #include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "hlwq.h"
 #include "hlwq_tables.inc"
@@ -1532,6 +1534,39 @@ bool mul_ok(int64_t a, int64_t b, int64_t* r) { return !__builtin_mul_overflow(a
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// One buffer of a call: the bytes [lo, hi) of `count` items of `unit` bytes
+// at p, and whether the call writes it (a size past the address space counts
+// as reaching its end).
+struct Span {
+  uintptr_t lo, hi;
+  bool written;
+};
+void add_span(std::vector<Span>& v, const void* p, int64_t count, int64_t unit, bool written) {
+  int64_t bytes;
+  if (!p || count <= 0) return;
+  if (!mul_ok(count, unit, &bytes)) bytes = INT64_MAX;
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  uintptr_t hi;
+  if (__builtin_add_overflow(lo, static_cast<uintptr_t>(bytes), &hi)) hi = UINTPTR_MAX;
+  v.push_back(Span{lo, hi, written});
+}
+
+// HLWQ_ERR_OVERLAP if a buffer the call writes shares a byte with any other
+// buffer of the call; buffers it only reads may overlap each other.  Sorted by
+// start, a span overlaps an earlier one exactly when it starts before that
+// one's end, so one pass with the running ends of all spans and of the
+// written ones decides.
+int check_disjoint(std::vector<Span>& v) {
+  std::sort(v.begin(), v.end(), [](const Span& a, const Span& b) { return a.lo < b.lo; });
+  uintptr_t end_any = 0, end_written = 0;
+  for (const Span& x : v) {
+    if (x.lo < end_written || (x.written && x.lo < end_any)) return HLWQ_ERR_OVERLAP;
+    end_any = std::max(end_any, x.hi);
+    if (x.written) end_written = std::max(end_written, x.hi);
+  }
+  return HLWQ_OK;
+}
+
 int launch_status() {
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? HLWQ_OK : HLWQ_ERR_DEVICE;
@@ -1600,11 +1635,17 @@ int run_weight_group(const hlwq_mat_desc* mats, int n, int bits, int field, hipS
   if (tq && (bits != 3 || field != 3)) return HLWQ_ERR_BITS;
   const int norm_bytes = tq ? 4 : 2;
   // validate everything before enqueuing anything
+  std::vector<Span> spans;
   for (int i = 0; i < n; ++i) {
     int64_t b;
     const int st = check_weight_desc(mats[i], &b, norm_bytes);
     if (st != HLWQ_OK) return st;
+    if (b == 0) continue;
+    add_span(spans, mats[i].w, mats[i].rows * mats[i].in, 2, !QUANT);
+    add_span(spans, mats[i].packed, b, 16 * field, QUANT);
+    add_span(spans, mats[i].norms, b, norm_bytes, QUANT);
   }
+  if (check_disjoint(spans) != HLWQ_OK) return HLWQ_ERR_OVERLAP;
   int i = 0;
   while (i < n) {
     WeightGroup g;
@@ -1744,6 +1785,11 @@ int run_kv(bool quant, const void* kv, void* packed, void* norms, int64_t batch,
   if ((reinterpret_cast<uintptr_t>(packed) & 15u) || (reinterpret_cast<uintptr_t>(norms) & 1u) ||
       (reinterpret_cast<uintptr_t>(kv) & 15u))
     return HLWQ_ERR_ALIGN;
+  std::vector<Span> spans;
+  add_span(spans, kv, bytes, 1, !quant);
+  add_span(spans, packed, nvec, 32 * bits, quant);
+  add_span(spans, norms, nvec, 2, quant);
+  if (check_disjoint(spans) != HLWQ_OK) return HLWQ_ERR_OVERLAP;
   KvArgs a;
   a.kv = const_cast<uint16_t*>(static_cast<const uint16_t*>(kv));
   a.packed = static_cast<uint8_t*>(packed);
@@ -1775,11 +1821,19 @@ int run_dequantize_int4(const hlwq_int4_desc* mats, int n, int bits, hipStream_t
   if (n < 0) return HLWQ_ERR_SHAPE;
   if (n > 0 && !mats) return HLWQ_ERR_NULL;
   if (bits != 5 && bits != 3) return HLWQ_ERR_BITS;
+  std::vector<Span> spans;
   for (int i = 0; i < n; ++i) {  // validate everything before enqueuing anything
     int64_t b;
     const int st = check_int4_desc(mats[i], &b);
     if (st != HLWQ_OK) return st;
+    if (b == 0) continue;
+    add_span(spans, mats[i].packed, b, 16 * bits, false);
+    add_span(spans, mats[i].norms, b, 2, false);
+    add_span(spans, mats[i].q4, b, kBlock / 2, true);
+    add_span(spans, mats[i].scales, b, 4, true);
+    add_span(spans, mats[i].zeros, b, 1, true);
   }
+  if (check_disjoint(spans) != HLWQ_OK) return HLWQ_ERR_OVERLAP;
   int i = 0;
   while (i < n) {
     Int4Group g;
@@ -1837,6 +1891,17 @@ int run_kv_append(const void* src, int64_t batch, int64_t heads, int64_t n_new, 
   // new tokens that arrive and leave within this call: rows tokens .. tokens + in_leaving - 1
   const int64_t in_leaving = n_new > n_residual ? n_new - n_residual : 0;
   if (bh > 0x3fffffff || in_leaving > 0x7fffffff) return HLWQ_ERR_LIMIT;
+  // checked last, after the launch limits of either path below
+  const auto overlap = [&]() {
+    std::vector<Span> spans;
+    add_span(spans, src, bytes, 1, false);
+    if (n_residual > 0) add_span(spans, ring, elems, 2 * kKvDim, true);
+    if (encodes) {
+      add_span(spans, packed, vecs, 32 * bits, true);
+      add_span(spans, norms, vecs, 2, true);
+    }
+    return check_disjoint(spans) != HLWQ_OK;
+  };
   KvAppendArgs a;
   a.src = static_cast<const uint16_t*>(src);
   a.ring = static_cast<uint16_t*>(ring);
@@ -1850,6 +1915,7 @@ int run_kv_append(const void* src, int64_t batch, int64_t heads, int64_t n_new, 
   if (n_new <= kSmallAppend) {
     // latency path: one wave per head
     if (bh > kMaxDispatch * kThreads / 64) return HLWQ_ERR_LIMIT;
+    if (overlap()) return HLWQ_ERR_OVERLAP;
     if (bits == 3) hipLaunchKernelGGL(hlwq_kv_append_small_kernel<3>, dim3(static_cast<uint32_t>(bh)), dim3(64), 0, stream, a);
     else hipLaunchKernelGGL(hlwq_kv_append_small_kernel<2>, dim3(static_cast<uint32_t>(bh)), dim3(64), 0, stream, a);
     return launch_status();
@@ -1860,6 +1926,7 @@ int run_kv_append(const void* src, int64_t batch, int64_t heads, int64_t n_new, 
   if (ceil_div(bh, kWaves) > kMaxDispatch || fill_groups > kMaxDispatch ||
       ceil_div(in_leaving, kKvTokens) > static_cast<int64_t>(kWaves) * kMaxDispatch)
     return HLWQ_ERR_LIMIT;
+  if (overlap()) return HLWQ_ERR_OVERLAP;
   if (in_leaving > 0) {
     // the streaming path's bulk (a prefill, say): the KV quantize kernel,
     // reading the new tokens and writing cache rows tokens .. leave_end - 1
@@ -2071,6 +2138,7 @@ const char* hlwq_status_string(int status) {
     case HLWQ_ERR_DEVICE: return "HIP launch failed";
     case HLWQ_ERR_ALIGN: return "buffer misaligned";
     case HLWQ_ERR_LIMIT: return "too many blocks for one call";
+    case HLWQ_ERR_OVERLAP: return "a buffer the call writes overlaps another of its buffers";
     default: return "unknown status";
   }
 }
