@@ -1567,9 +1567,21 @@ int check_disjoint(std::vector<Span>& v) {
   return HLWQ_OK;
 }
 
-int launch_status() {
-  const hipError_t e = hipGetLastError();
-  return e == hipSuccess ? HLWQ_OK : HLWQ_ERR_DEVICE;
+template <typename T>
+struct same_type {
+  using type = T;
+};
+
+// Launch a kernel and return the status of this launch itself (the runtime's
+// "last error" may hold an error some earlier, unrelated call left pending;
+// it is neither reported as ours nor cleared).  The arguments take the
+// kernel's own parameter types.
+template <typename... P>
+int launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream, typename same_type<P>::type... args) {
+  void* params[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, params, 0, stream) == hipSuccess
+             ? HLWQ_OK
+             : HLWQ_ERR_DEVICE;
 }
 
 // Validate one weight descriptor; *blocks = rows * nb (0 means nothing to do).
@@ -1683,34 +1695,21 @@ int run_weight_group(const hlwq_mat_desc* mats, int n, int bits, int field, hipS
                           : (g.total_batches + kDequantChunk - 1) / kDequantChunk),
         block(QUANT ? kPoolThreads : kThreads);
     const bool bytes = field == 8;
+    int st;
     if (tq) {
       // the recorded seed runs the kernels with the signs compiled in
       const bool seed42 = std::memcmp(tq, &kTq3Seed42, sizeof(TqSigns)) == 0;
-      if (QUANT) {
-        if (seed42) hipLaunchKernelGGL((hlwq_quantize_kernel<3, 3, 2>), grid, block, 0, stream, g);
-        else hipLaunchKernelGGL((hlwq_quantize_kernel<3, 3, 1>), grid, block, 0, stream, g);
-      } else {
-        if (seed42) hipLaunchKernelGGL((hlwq_dequantize_kernel<3, 3, 2>), grid, block, 0, stream, g);
-        else hipLaunchKernelGGL((hlwq_dequantize_kernel<3, 3, 1>), grid, block, 0, stream, g);
-      }
+      if (QUANT)
+        st = launch(seed42 ? hlwq_quantize_kernel<3, 3, 2> : hlwq_quantize_kernel<3, 3, 1>, grid, block, stream, g);
+      else
+        st = launch(seed42 ? hlwq_dequantize_kernel<3, 3, 2> : hlwq_dequantize_kernel<3, 3, 1>, grid, block, stream, g);
     } else if (QUANT) {
-      if (bits == 5) {
-        if (bytes) hipLaunchKernelGGL((hlwq_quantize_kernel<5, 8>), grid, block, 0, stream, g);
-        else hipLaunchKernelGGL((hlwq_quantize_kernel<5, 5>), grid, block, 0, stream, g);
-      } else {
-        if (bytes) hipLaunchKernelGGL((hlwq_quantize_kernel<3, 8>), grid, block, 0, stream, g);
-        else hipLaunchKernelGGL((hlwq_quantize_kernel<3, 3>), grid, block, 0, stream, g);
-      }
+      if (bits == 5) st = launch(bytes ? hlwq_quantize_kernel<5, 8> : hlwq_quantize_kernel<5, 5>, grid, block, stream, g);
+      else st = launch(bytes ? hlwq_quantize_kernel<3, 8> : hlwq_quantize_kernel<3, 3>, grid, block, stream, g);
     } else {
-      if (bits == 5) {
-        if (bytes) hipLaunchKernelGGL((hlwq_dequantize_kernel<5, 8>), grid, block, 0, stream, g);
-        else hipLaunchKernelGGL((hlwq_dequantize_kernel<5, 5>), grid, block, 0, stream, g);
-      } else {
-        if (bytes) hipLaunchKernelGGL((hlwq_dequantize_kernel<3, 8>), grid, block, 0, stream, g);
-        else hipLaunchKernelGGL((hlwq_dequantize_kernel<3, 3>), grid, block, 0, stream, g);
-      }
+      if (bits == 5) st = launch(bytes ? hlwq_dequantize_kernel<5, 8> : hlwq_dequantize_kernel<5, 5>, grid, block, stream, g);
+      else st = launch(bytes ? hlwq_dequantize_kernel<3, 8> : hlwq_dequantize_kernel<3, 3>, grid, block, stream, g);
     }
-    const int st = launch_status();
     if (st != HLWQ_OK) return st;
   }
   return HLWQ_OK;
@@ -1756,14 +1755,10 @@ int launch_kv(bool quant, int bits, KvArgs a, int64_t bh, hipStream_t stream) {
     l.total_batches = static_cast<uint32_t>(nh * a.nbt);
     const dim3 grid(quant ? persistent_grid(l.total_batches, 1, kKvPoolWaves) : (l.total_batches + l.chunk - 1) / l.chunk),
         block(quant ? kKvPoolThreads : kThreads);
-    if (quant) {
-      if (bits == 3) hipLaunchKernelGGL(hlwq_kv_quantize_kernel<3>, grid, block, 0, stream, l);
-      else hipLaunchKernelGGL(hlwq_kv_quantize_kernel<2>, grid, block, 0, stream, l);
-    } else {
-      if (bits == 3) hipLaunchKernelGGL(hlwq_kv_dequantize_kernel<3>, grid, block, 0, stream, l);
-      else hipLaunchKernelGGL(hlwq_kv_dequantize_kernel<2>, grid, block, 0, stream, l);
-    }
-    const int st = launch_status();
+    const int st = quant ? launch(bits == 3 ? hlwq_kv_quantize_kernel<3> : hlwq_kv_quantize_kernel<2>, grid, block,
+                                  stream, l)
+                         : launch(bits == 3 ? hlwq_kv_dequantize_kernel<3> : hlwq_kv_dequantize_kernel<2>, grid, block,
+                                  stream, l);
     if (st != HLWQ_OK) return st;
   }
   return HLWQ_OK;
@@ -1859,9 +1854,8 @@ int run_dequantize_int4(const hlwq_int4_desc* mats, int n, int bits, hipStream_t
     g.batch_start[g.n] = static_cast<uint32_t>(batches);
     g.total_batches = static_cast<uint32_t>(batches);
     const dim3 grid(persistent_grid(g.total_batches)), block_dim(kThreads);
-    if (bits == 5) hipLaunchKernelGGL(hlwq_dequantize_int4_kernel<5>, grid, block_dim, 0, stream, g);
-    else hipLaunchKernelGGL(hlwq_dequantize_int4_kernel<3>, grid, block_dim, 0, stream, g);
-    const int st = launch_status();
+    const int st = launch(bits == 5 ? hlwq_dequantize_int4_kernel<5> : hlwq_dequantize_int4_kernel<3>, grid,
+                          block_dim, stream, g);
     if (st != HLWQ_OK) return st;
   }
   return HLWQ_OK;
@@ -1916,9 +1910,8 @@ int run_kv_append(const void* src, int64_t batch, int64_t heads, int64_t n_new, 
     // latency path: one wave per head
     if (bh > kMaxDispatch * kThreads / 64) return HLWQ_ERR_LIMIT;
     if (overlap()) return HLWQ_ERR_OVERLAP;
-    if (bits == 3) hipLaunchKernelGGL(hlwq_kv_append_small_kernel<3>, dim3(static_cast<uint32_t>(bh)), dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL(hlwq_kv_append_small_kernel<2>, dim3(static_cast<uint32_t>(bh)), dim3(64), 0, stream, a);
-    return launch_status();
+    return launch(bits == 3 ? hlwq_kv_append_small_kernel<3> : hlwq_kv_append_small_kernel<2>,
+                  dim3(static_cast<uint32_t>(bh)), dim3(64), stream, a);
   }
   // everything is checked before the first launch
   const int64_t staying = n_new < n_residual ? n_new : n_residual;  // new tokens that stay in the window
@@ -1945,17 +1938,14 @@ int run_kv_append(const void* src, int64_t batch, int64_t heads, int64_t n_new, 
   if (leave_begin < (leave_end < tokens ? leave_end : tokens)) {
     // ring tokens leave: one wave per head encodes them
     const dim3 grid(static_cast<uint32_t>(ceil_div(bh, kWaves))), block(kThreads);
-    if (bits == 3) hipLaunchKernelGGL(hlwq_kv_append_kernel<3>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(hlwq_kv_append_kernel<2>, grid, block, 0, stream, a);
-    const int st = launch_status();
+    const int st = launch(bits == 3 ? hlwq_kv_append_kernel<3> : hlwq_kv_append_kernel<2>, grid, block, stream, a);
     if (st != HLWQ_OK) return st;
   }
   // then the new tokens that stay are written into the ring
   const int64_t t0 = leave_end > tokens ? leave_end : tokens;
   const int64_t ntok = total - t0;
-  hipLaunchKernelGGL(hlwq_kv_ring_fill_kernel, dim3(static_cast<uint32_t>(fill_groups)), dim3(kThreads), 0, stream, a,
-                     t0, ntok, t0 % n_residual);
-  return launch_status();
+  return launch(hlwq_kv_ring_fill_kernel, dim3(static_cast<uint32_t>(fill_groups)), dim3(kThreads), stream, a, t0, ntok,
+                t0 % n_residual);
 }
 
 }  // namespace

@@ -135,11 +135,13 @@ extern "C" int hlwq_stream_mix(const void* src, void* dst, uint32_t read_bytes, 
   const hipStream_t s = static_cast<hipStream_t>(hip_stream);
   const uint8_t* in = static_cast<const uint8_t*>(src);
   uint8_t* out = static_cast<uint8_t*>(dst);
-  switch (variant) {
-    case 0: hipLaunchKernelGGL((stream_mix_kernel<16384, false>), grid, block, 0, s, in, out, read_bytes, write_bytes, units); break;
-    case 1: hipLaunchKernelGGL((stream_mix_kernel<32768, false>), grid, block, 0, s, in, out, read_bytes, write_bytes, units); break;
-    case 2: hipLaunchKernelGGL((stream_mix_kernel<32768, true>), grid, block, 0, s, in, out, read_bytes, write_bytes, units); break;
-    default: hipLaunchKernelGGL((stream_mix_kernel<8192, true>), grid, block, 0, s, in, out, read_bytes, write_bytes, units); break;
-  }
-  return hipGetLastError() == hipSuccess ? 0 : -5;
+  using Kernel = void (*)(const uint8_t*, uint8_t*, uint32_t, uint32_t, uint32_t);
+  static const Kernel kernels[4] = {stream_mix_kernel<16384, false>, stream_mix_kernel<32768, false>,
+                                    stream_mix_kernel<32768, true>, stream_mix_kernel<8192, true>};
+  uint32_t rb = read_bytes, wb = write_bytes, n = units;
+  void* params[] = {&in, &out, &rb, &wb, &n};
+  // the status of this launch itself, not an error an earlier call left pending
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernels[variant]), grid, block, params, 0, s) == hipSuccess
+             ? 0
+             : -5;
 }
