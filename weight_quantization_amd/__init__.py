@@ -31,4 +31,5 @@ from .binding import (  # noqa: F401
     hlwq_tq3_quantize_grouped,
     hlwq_tq3_signs,
     load_library,
+    packed_shape,
 )
