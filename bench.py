@@ -52,6 +52,9 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+# VALU issue peak for unpacked fp32 / integer ops: 256 CUs x 4 SIMDs x 16 lanes
+# x 2.4 GHz = 39.3 T lane-ops/s (a wave64 instruction takes 4 cycles on a SIMD)
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 METRIC = "weights/s and achieved HBM GB/s (% of peak) for Q5 quantize+dequantize"
 
 DESCRIPTIONS = {
@@ -687,10 +690,21 @@ def time_workload(torch, wl, steps, warmup):
     return q_ms, d_ms, wall
 
 
-def leg(ms, nbytes, weights, ceiling):
+def valu_rate(ops_per_value, values, ms):
+    """VALU lane-ops per second of a leg (the committed per-value instruction
+    count x 64 lanes, over the live kernel time) against the VALU issue peak."""
+    if ops_per_value is None:
+        return None
+    tops = ops_per_value * values / (ms * 1e-3) / 1e12
+    return {"achieved": round(tops, 2), "peak": round(VALU_PEAK_TOPS, 2), "unit": "T VALU lane-ops/s",
+            "frac": round(tops / VALU_PEAK_TOPS, 4)}
+
+
+def leg(ms, nbytes, weights, ceiling, ops_per_value=None):
     """Timing summary of one kernel (leg of the step): GB/s are algorithmic
     bytes over the mean time; fractions of the 8 TB/s peak and of the
-    streaming ceiling of the same read:write mix."""
+    streaming ceiling of the same read:write mix; with the committed VALU
+    count per value, the fraction of the VALU issue peak."""
     gbs = nbytes / (ms.mean() * 1e-3) / 1e9
     out = {"ms": round(float(ms.mean()), 4), "ms_median": round(float(np.median(ms)), 4),
            "ms_min": round(float(ms.min()), 4), "ms_max": round(float(ms.max()), 4),
@@ -698,6 +712,8 @@ def leg(ms, nbytes, weights, ceiling):
     if ceiling is not None:
         out["ceiling_gbs"] = ceiling["gbs"]
         out["frac_of_ceiling"] = round(gbs / ceiling["gbs"], 4)
+    if ops_per_value is not None:
+        out["valu"] = valu_rate(ops_per_value, weights, float(ms.mean()))
     return out
 
 
@@ -721,15 +737,16 @@ def extra_bank(torch, wq, dev, ceil, config, bits, steps, warmup):
     q_ms, d_ms, wall = time_workload(torch, wl, steps, warmup)
     weights, nbytes = wl["weights"], wl["bytes"]
     step_gbs = 2 * nbytes / (wall / steps) / 1e9
+    valu = stored_valu(config, bits)
     out = {"workload": DESCRIPTIONS[config], "weights": weights, "bits": bits, "steps": steps, "warmup": warmup,
            "algorithmic_bytes_per_launch": nbytes, "ms_per_step": round(wall * 1e3 / steps, 4),
            "weights_per_s": weights / (wall / steps), "hbm_gbs": round(step_gbs, 1),
            "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
            "settle": {"seconds": SETTLE_S, "steps": n_settle},
-           "quantize": leg(q_ms, nbytes, weights, c["quantize_mix"]),
-           "dequantize": leg(d_ms, nbytes, weights, c["dequantize_mix"]),
+           "quantize": leg(q_ms, nbytes, weights, c["quantize_mix"], (valu or {}).get("quantize")),
+           "dequantize": leg(d_ms, nbytes, weights, c["dequantize_mix"], (valu or {}).get("dequantize")),
            "traffic": stored_traffic(config, bits),
-           "valu_ops_per_value": stored_valu(config, bits),
+           "valu_ops_per_value": valu,
            "ceiling": c}
     del wl
     torch.cuda.empty_cache()
@@ -812,6 +829,7 @@ def main():
     dom_bytes, dom_launches = (bytes_dir, launches) if dom == 0 else (bytes_d, launches_d)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = stored_traffic(config, bits) if args.layout == "packed" else None
+    valu = stored_valu(config, bits) if args.layout == "packed" else None
     roofline = {
         "bound": "hbm",
         "kernel": wl["kernels"][dom] + ("" if dom_launches == 1 else f" ({dom_launches} launches per step)"),
@@ -823,6 +841,10 @@ def main():
                     traffic["quantize_bytes_per_launch" if dom == 0 else "dequantize_bytes_per_launch"]),
         "algorithmic_bytes_per_launch": dom_bytes // dom_launches,
         "avg_launch_ms": round(dom_ms / dom_launches, 4),
+        # the same kernel against the VALU issue peak (from the committed
+        # instruction count per value; null without one for this source)
+        "valu": valu_rate(None if valu is None else valu["quantize" if dom == 0 else "dequantize"], weights,
+                          float(dom_ms)),
     }
     step_gbs = (bytes_dir + bytes_d) / (ms_per_step * 1e-3) / 1e9
     result = {
@@ -849,12 +871,12 @@ def main():
         # untimed steps run before the W warm-up steps, until the card's
         # clocks have settled (see settle())
         "settle": {"seconds": SETTLE_S, "steps": n_settle},
-        "quantize": leg(q_ms, bytes_dir, weights, ceiling["quantize_mix"]),
-        "dequantize": leg(d_ms, bytes_d, weights, ceiling["dequantize_mix"]),
+        "quantize": leg(q_ms, bytes_dir, weights, ceiling["quantize_mix"], (valu or {}).get("quantize")),
+        "dequantize": leg(d_ms, bytes_d, weights, ceiling["dequantize_mix"], (valu or {}).get("dequantize")),
         "roofline": roofline,
         # VALU instructions per quantised value from the committed counters
         # (null when they were taken on other kernel source)
-        "valu_ops_per_value": stored_valu(config, bits) if args.layout == "packed" else None,
+        "valu_ops_per_value": valu,
         "ceiling": ceiling,
     }
     del wl

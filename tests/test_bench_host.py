@@ -50,3 +50,14 @@ def test_committed_counters_are_read_only_for_the_current_kernel_source(tmp_path
     assert bench.stored_valu("z", 5) is None          # no summary
     assert bench.stored_traffic("z", 5) is None
 
+
+
+def test_valu_rate_against_the_issue_peak():
+    # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+    assert abs(bench.VALU_PEAK_TOPS - 39.3216) < 1e-9
+    # 16 ops per value over 2.4576e9 values in 1 ms: 39.3216 T lane-ops/s, the peak
+    r = bench.valu_rate(16.0, 2_457_600_000, 1.0)
+    assert r["unit"] == "T VALU lane-ops/s" and abs(r["achieved"] - 39.32) < 0.01 and abs(r["frac"] - 1.0) < 1e-4
+    r = bench.valu_rate(15.06, 805_306_368, 0.378)
+    assert abs(r["achieved"] - 15.06 * 805_306_368 / 0.378e-3 / 1e12) < 0.01
+    assert bench.valu_rate(None, 1, 1.0) is None
