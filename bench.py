@@ -700,6 +700,20 @@ def valu_rate(ops_per_value, values, ms):
             "frac": round(tops / VALU_PEAK_TOPS, 4)}
 
 
+def roofline_of(kernel, gbs, ceiling_gbs, valu):
+    """The roofline of the dominant kernel.  It is HBM-bound ("hbm": algorithmic
+    GB/s against 8 TB/s) unless it uses more of the VALU issue peak than of the
+    measured streaming rate of its own read:write mix; then it is bound by
+    VALU issue ("alu": lane-ops/s against the peak), and the HBM figures are
+    kept under "hbm".  Without a committed VALU count it is "hbm"."""
+    hbm = {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+           "frac_of_ceiling": round(gbs / ceiling_gbs, 4)}
+    if valu is not None and valu["frac"] > gbs / ceiling_gbs:
+        return {"bound": "alu", "kernel": kernel, **{k: valu[k] for k in ("achieved", "peak", "unit", "frac")},
+                "hbm": hbm}
+    return {"bound": "hbm", "kernel": kernel, **hbm, "valu": valu}
+
+
 def leg(ms, nbytes, weights, ceiling, ops_per_value=None):
     """Timing summary of one kernel (leg of the step): GB/s are algorithmic
     bytes over the mean time; fractions of the 8 TB/s peak and of the
@@ -830,22 +844,16 @@ def main():
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = stored_traffic(config, bits) if args.layout == "packed" else None
     valu = stored_valu(config, bits) if args.layout == "packed" else None
-    roofline = {
-        "bound": "hbm",
-        "kernel": wl["kernels"][dom] + ("" if dom_launches == 1 else f" ({dom_launches} launches per step)"),
-        "achieved": round(achieved, 1),
-        "peak": HBM_PEAK_GBS,
-        "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4),
+    roofline = roofline_of(wl["kernels"][dom] + ("" if dom_launches == 1 else f" ({dom_launches} launches per step)"),
+                           achieved, ceiling["quantize_mix" if dom == 0 else "dequantize_mix"]["gbs"],
+                           valu_rate(None if valu is None else valu["quantize" if dom == 0 else "dequantize"],
+                                     weights, float(dom_ms)))
+    roofline.update({
         "traffic": (None if traffic is None else
                     traffic["quantize_bytes_per_launch" if dom == 0 else "dequantize_bytes_per_launch"]),
         "algorithmic_bytes_per_launch": dom_bytes // dom_launches,
         "avg_launch_ms": round(dom_ms / dom_launches, 4),
-        # the same kernel against the VALU issue peak (from the committed
-        # instruction count per value; null without one for this source)
-        "valu": valu_rate(None if valu is None else valu["quantize" if dom == 0 else "dequantize"], weights,
-                          float(dom_ms)),
-    }
+    })
     step_gbs = (bytes_dir + bytes_d) / (ms_per_step * 1e-3) / 1e9
     result = {
         "metric": METRIC,

@@ -61,3 +61,15 @@ def test_valu_rate_against_the_issue_peak():
     r = bench.valu_rate(15.06, 805_306_368, 0.378)
     assert abs(r["achieved"] - 15.06 * 805_306_368 / 0.378e-3 / 1e12) < 0.01
     assert bench.valu_rate(None, 1, 1.0) is None
+
+
+def test_roofline_is_the_more_used_of_memory_and_valu():
+    valu_low = {"achieved": 18.7, "peak": 39.32, "unit": "T VALU lane-ops/s", "frac": 0.476}
+    r = bench.roofline_of("dequantize", 5536.7, 5540.2, valu_low)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["frac"] == round(5536.7 / 8000, 4)
+    assert r["valu"] == valu_low and r["frac_of_ceiling"] == round(5536.7 / 5540.2, 4)
+    valu_high = {"achieved": 34.2, "peak": 39.32, "unit": "T VALU lane-ops/s", "frac": 0.87}
+    r = bench.roofline_of("kv quantize", 4920.0, 5900.0, valu_high)
+    assert r["bound"] == "alu" and r["frac"] == 0.87 and r["unit"] == "T VALU lane-ops/s"
+    assert r["hbm"]["achieved"] == 4920.0 and r["hbm"]["frac"] == round(4920.0 / 8000, 4)
+    assert bench.roofline_of("x", 4000.0, 5000.0, None)["bound"] == "hbm"
