@@ -260,6 +260,43 @@ def test_grouped_launch_splits(wq):
         assert np.array_equal(bf16_bits(o), ref.dequantize_c(op, on, wb.shape[1], 5))
 
 
+@pytest.mark.parametrize("count", [1, 16, 17, 32, 33])
+@pytest.mark.parametrize("bits", [5, 3])
+def test_grouped_launch_descriptor_counts(wq, bits, count):
+    # `count` non-empty matrices, with empty ones (0 rows or 0 columns, which
+    # take no slot of a launch) between them: one launch holds 16, so 16 and
+    # 32 fill their launches exactly and 17 and 33 leave one matrix for the
+    # next.  Every matrix equal to the oracle after quantize and dequantize.
+    rng = np.random.default_rng(900 + 10 * bits + count)
+    items, host = [], []
+    for i in range(count):
+        if i % 5 == 2:  # an empty matrix before this one
+            e = torch.empty((0, 256) if i % 2 else (7, 0), dtype=torch.bfloat16, device="cuda")
+            ps, ns = wq.packed_shape(tuple(e.shape), bits)
+            items.append((e, torch.empty(ps, dtype=torch.uint8, device="cuda"),
+                          torch.empty(ns, dtype=torch.float16, device="cuda")))
+            host.append(None)
+        rows = int(rng.integers(1, 40))
+        n_in = int(rng.choice([8, 64, 128, 200, 704]))
+        wb = synth.random_bf16((rows, n_in), seed=1000 * bits + 37 * count + i)
+        ps, ns = wq.packed_shape((rows, n_in), bits)
+        items.append((to_dev(wb), torch.empty(ps, dtype=torch.uint8, device="cuda"),
+                      torch.empty(ns, dtype=torch.float16, device="cuda")))
+        host.append(wb)
+    _say("grouped launch", count, "matrices, bits", bits)
+    wq.hlwq_quantize_grouped(items, bits)
+    outs = [(torch.empty_like(w), p, n) for (w, p, n) in items]
+    wq.hlwq_dequantize_grouped(outs, bits)
+    torch.cuda.synchronize()
+    for (w, p, n), (o, _, _), wb in zip(items, outs, host):
+        if wb is None:
+            continue
+        op, on = ref.quantize_c(wb, bits)
+        assert np.array_equal(p.cpu().numpy(), op)
+        assert np.array_equal(f16_bits(n), on.view(np.uint16))
+        assert np.array_equal(bf16_bits(o), ref.dequantize_c(op, on, wb.shape[1], bits))
+
+
 @pytest.mark.parametrize("bits", [5, 3])
 def test_grouped_launch_mixed_paths(wq, bits):
     # one grouped launch whose matrices take every read path: whole aligned
