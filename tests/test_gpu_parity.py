@@ -518,6 +518,28 @@ def test_kv_batches_per_head(wq, nbt):
     assert np.all(got[:, :, tq:] == 0x3F80)
 
 
+@pytest.mark.parametrize("bits", [3, 2])
+@pytest.mark.parametrize("tq", [1, 15, 16, 17, 31, 32, 33])
+def test_kv_token_counts_at_batch_edges(wq, bits, tq):
+    # quantised tokens per head just below, at and above multiples of the
+    # 16-token batch, behind a 100-token window: last batches of 1, 15 and 16
+    # tokens; 3 heads x 2 batch entries, so heads start mid-launch
+    B, H, T = 2, 3, tq + 100
+    kv = synth.random_bf16((B, H, T, 256), seed=4000 + 10 * tq + bits, sigma=1.0)
+    _say("kv batch edges", tq, "bits", bits)
+    dev = to_dev(kv)
+    packed, norms = wq.hlwq_kv_quantize(dev, n_residual=100, bits=bits)
+    out = to_dev(np.full((B, H, T, 256), 0x3F80, np.uint16))
+    wq.hlwq_kv_dequantize(packed, norms, out, n_residual=100, bits=bits)
+    torch.cuda.synchronize()
+    op, on = ref.kv_quantize_c(kv, n_residual=100, bits=bits)
+    assert np.array_equal(packed.cpu().numpy(), op)
+    assert np.array_equal(f16_bits(norms), on.view(np.uint16))
+    got = bf16_bits(out)
+    assert np.array_equal(got[:, :, :tq], ref.kv_dequantize_c(op, on, bits=bits))
+    assert np.all(got[:, :, tq:] == 0x3F80)
+
+
 @pytest.mark.parametrize("shape", [(1, 2, 300), (2, 3, 129), (1, 1, 1000)])
 def test_kv_cache_q2(wq, shape):
     B, H, T = shape
