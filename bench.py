@@ -600,8 +600,8 @@ def _pool_map(n, args):
         pool.join()
 
 
-# One GPU's share of a GPU machine's host is 16 cores, whatever the affinity mask
-# shows; the pool uses every core of the mask up to that share.
+# One GPU's share of an 8-GPU MI355X host's CPU cores is 16, whatever the
+# affinity mask shows; the pool uses every core of the mask up to that share.
 HOST_SHARE_CORES = 16
 
 
